@@ -1,0 +1,215 @@
+"""ctypes binding of libsolattn.so (the C ABI declared in include/sol_attn.h).
+
+Argument marshalling only: every step of the attention runs in the HIP
+kernels of the library. Tensors are torch tensors on a ROCm device, used for
+device memory and streams. There is no fallback: if the library is missing
+or fails, these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Dict, Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsolattn.so")
+
+SOL_OK = 0
+SOL_ERR_INVALID_ARG = 1
+SOL_ERR_UNSUPPORTED = 2
+SOL_ERR_DEVICE = 3
+SOL_ERR_NOMEM = 4
+SOL_ERR_WORKSPACE = 5
+
+SOL_BF16 = 0x0
+SOL_F32 = 0x1
+SOL_CORRECTION = 0x2
+SOL_DENSE = 0x4
+SOL_SYNC = 0x8
+
+BLOCK = 64
+
+
+class SolError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"sol_attn status {status}: {message}")
+        self.status = status
+
+
+class sol_debug(ctypes.Structure):
+    _fields_ = [("kept_per_row", ctypes.c_void_p),
+                ("mask_bits", ctypes.c_void_p),
+                ("tau", ctypes.c_void_p)]
+
+
+class sol_workspace_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("total_bytes", "kbar_t", "kbar", "vsum", "kmean", "kcov", "scratch")]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsolattn.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m free_block_sparse_mean_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, u, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint, ctypes.c_size_t
+    lib.sol_abi_version.argtypes = []
+    lib.sol_abi_version.restype = i
+    lib.sol_last_error.argtypes = []
+    lib.sol_last_error.restype = ctypes.c_char_p
+    lib.sol_attn_workspace_bytes.argtypes = [i, i, i, i]
+    lib.sol_attn_workspace_bytes.restype = sz
+    lib.sol_attn_workspace_layout.argtypes = [i, i, i, i, ctypes.POINTER(sol_workspace_layout)]
+    lib.sol_attn_workspace_layout.restype = i
+    lib.sol_block_summaries.argtypes = [vp, vp, i, i, i, i, u, vp, sz, vp]
+    lib.sol_block_summaries.restype = i
+    lib.sol_attn_fused.argtypes = [vp, vp, vp, vp, i, i, i, i, f, u, vp, sz,
+                                   ctypes.POINTER(sol_debug), vp]
+    lib.sol_attn_fused.restype = i
+    lib.sol_attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, f, u, vp, vp, sz,
+                                    ctypes.POINTER(sol_debug)]
+    lib.sol_attn_fwd_ex.restype = i
+    lib.sol_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, f, u]
+    lib.sol_attn_fwd.restype = i
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != SOL_OK:
+        raise SolError(status, sol_last_error())
+
+
+def sol_abi_version() -> int:
+    return load_library().sol_abi_version()
+
+
+def sol_last_error() -> str:
+    return load_library().sol_last_error().decode()
+
+
+def sol_attn_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return load_library().sol_attn_workspace_bytes(B, H, N, d)
+
+
+def sol_attn_workspace_layout(B: int, H: int, N: int, d: int) -> sol_workspace_layout:
+    lay = sol_workspace_layout()
+    _check(load_library().sol_attn_workspace_layout(B, H, N, d, ctypes.byref(lay)))
+    return lay
+
+
+def _shape(q: torch.Tensor):
+    if q.dim() != 4:
+        raise ValueError("tensors must be [B, H, N, d]")
+    return tuple(int(x) for x in q.shape)
+
+
+def _dtype_flag(*ts: torch.Tensor) -> int:
+    dts = {t.dtype for t in ts}
+    if dts == {torch.bfloat16}:
+        return SOL_BF16
+    if dts == {torch.float32}:
+        return SOL_F32
+    raise ValueError(f"all tensors must be bfloat16 or all float32, got {dts}")
+
+
+def _dev(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dbg(kept_per_row=None, mask_bits=None, tau=None):
+    if kept_per_row is None and mask_bits is None and tau is None:
+        return None
+    ptr = lambda t: None if t is None else t.data_ptr()
+    return ctypes.byref(sol_debug(ptr(kept_per_row), ptr(mask_bits), ptr(tau)))
+
+
+def new_workspace(B: int, H: int, N: int, d: int, device=None) -> torch.Tensor:
+    """A uint8 device tensor of sol_attn_workspace_bytes bytes."""
+    n = sol_attn_workspace_bytes(B, H, N, d)
+    if n == 0:
+        raise ValueError("invalid or unsupported shape")
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def workspace_views(ws: torch.Tensor, B: int, H: int, N: int, d: int) -> Dict[str, torch.Tensor]:
+    """Typed views of the pre-pass arrays inside a workspace tensor."""
+    lay = sol_attn_workspace_layout(B, H, N, d)
+    nb = N // BLOCK
+    nbp = (nb + 3) // 4 * 4
+    f32 = lambda off, shape: ws[off:off + 4 * math.prod(shape)].view(torch.float32).view(shape)
+    return {
+        "kbar_t": f32(lay.kbar_t, (B, H, d, nbp))[..., :nb],
+        "kbar": f32(lay.kbar, (B, H, nb, d)),
+        "vsum": f32(lay.vsum, (B, H, nb, d)),
+        "kmean": f32(lay.kmean, (B, H, d)),
+        "kcov": f32(lay.kcov, (B, H, d, d)),
+    }
+
+
+def sol_block_summaries(k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor,
+                        flags: int = 0, stream=None) -> None:
+    _dev(k, v, workspace)
+    B, H, N, d = _shape(k)
+    flags |= _dtype_flag(k, v)
+    _check(load_library().sol_block_summaries(k.data_ptr(), v.data_ptr(), B, H, N, d, flags,
+                                              workspace.data_ptr(), workspace.numel(),
+                                              _stream(stream)))
+
+
+def sol_attn_fused(q, k, v, out, beta: float, flags: int, workspace: torch.Tensor, *,
+                   kept_per_row=None, mask_bits=None, tau=None, stream=None) -> None:
+    _dev(q, k, v, out, workspace)
+    B, H, N, d = _shape(q)
+    flags |= _dtype_flag(q, k, v, out)
+    _check(load_library().sol_attn_fused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         B, H, N, d, float(beta), flags, workspace.data_ptr(),
+                                         workspace.numel(), _dbg(kept_per_row, mask_bits, tau),
+                                         _stream(stream)))
+
+
+def sol_attn_fwd_ex(q, k, v, out, beta: float, flags: int, stream=None,
+                    workspace: Optional[torch.Tensor] = None, *, kept_per_row=None,
+                    mask_bits=None, tau=None) -> None:
+    _dev(q, k, v, out)
+    B, H, N, d = _shape(q)
+    flags |= _dtype_flag(q, k, v, out)
+    if workspace is None:
+        workspace = new_workspace(B, H, N, d, q.device)
+    _check(load_library().sol_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                          B, H, N, d, float(beta), flags, _stream(stream),
+                                          workspace.data_ptr(), workspace.numel(),
+                                          _dbg(kept_per_row, mask_bits, tau)))
+
+
+def sol_attn_fwd(q, k, v, out, beta: float, flags: int) -> None:
+    _dev(q, k, v, out)
+    B, H, N, d = _shape(q)
+    flags |= _dtype_flag(q, k, v, out)
+    _check(load_library().sol_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       B, H, N, d, float(beta), flags))
+
+
+def decode_mask(mask_bits: torch.Tensor, n_b: int) -> torch.Tensor:
+    """[..., W] int64 words -> [..., n_b] bool (bit j%64 of word j//64)."""
+    words = mask_bits.cpu()
+    bits = torch.arange(64, dtype=torch.int64)
+    m = ((words.unsqueeze(-1) >> bits) & 1).bool()
+    return m.reshape(*words.shape[:-1], -1)[..., :n_b]

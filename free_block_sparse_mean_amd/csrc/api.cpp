@@ -1,0 +1,265 @@
+// C-ABI host runtime of the Sol-Attn library: argument validation (before any
+// device call), workspace layout, the library-owned workspace of sol_attn_fwd,
+// HIP error -> sol_status mapping and the per-thread error message.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/sol_attn.h"
+#include "sol_internal.hpp"
+
+namespace sol {
+
+static size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Layout make_layout(const Shape& s) {
+  const size_t bh = (size_t)s.BH(), d = (size_t)s.d, nb = (size_t)s.n_b;
+  Layout L;
+  size_t off = 0;
+  L.kbar_t = off;   off += up256(bh * d * (size_t)s.n_b_pad * 4);
+  L.kbar = off;     off += up256(bh * nb * d * 4);
+  L.vsum = off;     off += up256(bh * nb * d * 4);
+  L.kmean = off;    off += up256(bh * d * 4);
+  L.kcov = off;     off += up256(bh * d * d * 4);
+  L.kmean64 = off;  off += up256(bh * d * 8);
+  L.cov_part = off; off += up256(bh * (size_t)s.cov_parts * d * d * 8);
+  L.total = off;
+  return L;
+}
+
+Workspace bind_workspace(const Shape& s, void* base) {
+  const Layout L = make_layout(s);
+  char* b = static_cast<char*>(base);
+  Workspace w;
+  w.kbar_t = reinterpret_cast<float*>(b + L.kbar_t);
+  w.kbar = reinterpret_cast<float*>(b + L.kbar);
+  w.vsum = reinterpret_cast<float*>(b + L.vsum);
+  w.kmean = reinterpret_cast<float*>(b + L.kmean);
+  w.kcov = reinterpret_cast<float*>(b + L.kcov);
+  w.kmean64 = reinterpret_cast<double*>(b + L.kmean64);
+  w.cov_part = reinterpret_cast<double*>(b + L.cov_part);
+  return w;
+}
+
+}  // namespace sol
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sol_status fail(sol_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sol_status ok() {
+  g_err[0] = '\0';
+  return SOL_OK;
+}
+
+sol_status device_fail(hipError_t e, const char* what) {
+  return fail(SOL_ERR_DEVICE, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+// Shape checks shared by every entry point; fills `s` on success.
+sol_status check_shape(int B, int H, int N, int d, sol::Shape* s) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0)
+    return fail(SOL_ERR_INVALID_ARG, "B, H, N, d must be positive (got %d, %d, %d, %d)", B, H, N, d);
+  if (N % sol::kBlock != 0)
+    return fail(SOL_ERR_INVALID_ARG, "N = %d is not a multiple of the 64-token block", N);
+  if (d != 64 && d != 128)
+    return fail(SOL_ERR_UNSUPPORTED, "head dim d = %d is not supported (64 or 128)", d);
+  if (N / sol::kBlock > sol::kMaxBlocks)
+    return fail(SOL_ERR_UNSUPPORTED, "N = %d exceeds the supported maximum %d", N,
+                sol::kMaxBlocks * sol::kBlock);
+  if ((long long)B * H > 65535)
+    return fail(SOL_ERR_UNSUPPORTED, "B*H = %lld exceeds 65535", (long long)B * H);
+  s->B = B; s->H = H; s->N = N; s->d = d;
+  s->n_b = N / sol::kBlock;
+  s->n_b_pad = (s->n_b + 3) & ~3;
+  s->n_words = (s->n_b + 63) / 64;
+  s->cov_parts = (s->n_b + sol::kCovChunk - 1) / sol::kCovChunk;
+  if ((long long)B * H * s->n_b > 0x7fffffffLL)
+    return fail(SOL_ERR_UNSUPPORTED, "B*H*N/64 exceeds the launch grid limit");
+  return SOL_OK;
+}
+
+sol_status check_flags(unsigned flags) {
+  if (flags & ~SOL_FLAGS_ALL) return fail(SOL_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~SOL_FLAGS_ALL);
+  return SOL_OK;
+}
+
+sol::Dtype dtype_of(unsigned flags) { return (flags & SOL_F32) ? sol::Dtype::F32 : sol::Dtype::BF16; }
+
+sol_status finish(unsigned flags, hipStream_t st) {
+  if (flags & SOL_SYNC) {
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return device_fail(e, "hipStreamSynchronize");
+  }
+  return ok();
+}
+
+sol_status summaries_checked(const sol::Shape& s, const void* k, const void* v, unsigned flags,
+                             void* ws, hipStream_t st) {
+  const sol::Workspace w = sol::bind_workspace(s, ws);
+  hipError_t e = sol::launch_prepass(s, dtype_of(flags), k, v, w, st);
+  if (e != hipSuccess) return device_fail(e, "block-summary pre-pass launch");
+  return SOL_OK;
+}
+
+sol_status fused_checked(const sol::Shape& s, const void* q, const void* k, const void* v, void* out,
+                         float beta, unsigned flags, const void* ws, const sol_debug* dbg,
+                         hipStream_t st) {
+  sol::FusedArgs a;
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.ws = sol::bind_workspace(s, const_cast<void*>(ws));
+  a.beta = beta;
+  a.beta_mode = (flags & SOL_DENSE) || beta == -INFINITY ? sol::kBetaMinusInf
+                : beta == INFINITY                       ? sol::kBetaPlusInf
+                                                         : sol::kBetaFinite;
+  a.correction = (flags & SOL_CORRECTION) != 0;
+  a.kept_per_row = dbg ? dbg->kept_per_row : nullptr;
+  a.mask_bits = dbg ? dbg->mask_bits : nullptr;
+  a.tau = dbg ? dbg->tau : nullptr;
+  hipError_t e = sol::launch_fused(s, dtype_of(flags), a, st);
+  if (e != hipSuccess) return device_fail(e, "fused kernel launch");
+  return SOL_OK;
+}
+
+sol_status check_fused_args(const void* q, const void* k, const void* v, void* out, float beta,
+                            unsigned flags) {
+  if (!q || !k || !v || !out) return fail(SOL_ERR_INVALID_ARG, "q, k, v and out must be non-null");
+  if (isnan(beta)) return fail(SOL_ERR_INVALID_ARG, "beta is NaN");
+  return check_flags(flags);
+}
+
+// Library-owned workspace of sol_attn_fwd, one per device.
+struct OwnedWorkspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+// Held until the process ends (no hipFree from static destructors, which may
+// run after the HIP runtime has shut down).
+std::mutex g_ws_mutex;
+std::vector<OwnedWorkspace> g_ws;
+
+}  // namespace
+
+extern "C" {
+
+int sol_abi_version(void) { return SOL_ATTN_ABI_VERSION; }
+
+const char* sol_last_error(void) { return g_err; }
+
+size_t sol_attn_workspace_bytes(int B, int H, int N, int d) {
+  sol::Shape s;
+  char saved[sizeof(g_err)];
+  memcpy(saved, g_err, sizeof(g_err));
+  const sol_status st = check_shape(B, H, N, d, &s);
+  memcpy(g_err, saved, sizeof(g_err));
+  return st == SOL_OK ? sol::make_layout(s).total : 0;
+}
+
+sol_status sol_attn_workspace_layout(int B, int H, int N, int d, sol_workspace_layout* layout) {
+  if (!layout) return fail(SOL_ERR_INVALID_ARG, "layout must be non-null");
+  sol::Shape s;
+  sol_status st = check_shape(B, H, N, d, &s);
+  if (st != SOL_OK) return st;
+  const sol::Layout L = sol::make_layout(s);
+  layout->total_bytes = L.total;
+  layout->kbar_t = L.kbar_t;
+  layout->kbar = L.kbar;
+  layout->vsum = L.vsum;
+  layout->kmean = L.kmean;
+  layout->kcov = L.kcov;
+  layout->scratch = L.kmean64;
+  return ok();
+}
+
+sol_status sol_block_summaries(const void* k, const void* v, int B, int H, int N, int d,
+                               unsigned flags, void* workspace, size_t ws_bytes, void* hip_stream) {
+  sol::Shape s;
+  sol_status st = check_shape(B, H, N, d, &s);
+  if (st != SOL_OK) return st;
+  if (!k || !v) return fail(SOL_ERR_INVALID_ARG, "k and v must be non-null");
+  if ((st = check_flags(flags)) != SOL_OK) return st;
+  if (!workspace || ws_bytes < sol::make_layout(s).total)
+    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
+                ws_bytes, workspace ? "" : ", NULL");
+  hipStream_t str = static_cast<hipStream_t>(hip_stream);
+  if ((st = summaries_checked(s, k, v, flags, workspace, str)) != SOL_OK) return st;
+  return finish(flags, str);
+}
+
+sol_status sol_attn_fused(const void* q, const void* k, const void* v, void* out, int B, int H,
+                          int N, int d, float beta, unsigned flags, const void* workspace,
+                          size_t ws_bytes, const sol_debug* dbg, void* hip_stream) {
+  sol::Shape s;
+  sol_status st = check_shape(B, H, N, d, &s);
+  if (st != SOL_OK) return st;
+  if ((st = check_fused_args(q, k, v, out, beta, flags)) != SOL_OK) return st;
+  if (!workspace || ws_bytes < sol::make_layout(s).total)
+    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
+                ws_bytes, workspace ? "" : ", NULL");
+  hipStream_t str = static_cast<hipStream_t>(hip_stream);
+  if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str)) != SOL_OK) return st;
+  return finish(flags, str);
+}
+
+sol_status sol_attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int H,
+                           int N, int d, float beta, unsigned flags, void* hip_stream,
+                           void* workspace, size_t ws_bytes, const sol_debug* dbg) {
+  sol::Shape s;
+  sol_status st = check_shape(B, H, N, d, &s);
+  if (st != SOL_OK) return st;
+  if ((st = check_fused_args(q, k, v, out, beta, flags)) != SOL_OK) return st;
+  if (!workspace || ws_bytes < sol::make_layout(s).total)
+    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
+                ws_bytes, workspace ? "" : ", NULL");
+  hipStream_t str = static_cast<hipStream_t>(hip_stream);
+  if ((st = summaries_checked(s, k, v, flags, workspace, str)) != SOL_OK) return st;
+  if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str)) != SOL_OK) return st;
+  return finish(flags, str);
+}
+
+sol_status sol_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N,
+                        int d, float beta, unsigned flags) {
+  sol::Shape s;
+  sol_status st = check_shape(B, H, N, d, &s);
+  if (st != SOL_OK) return st;
+  if ((st = check_fused_args(q, k, v, out, beta, flags)) != SOL_OK) return st;
+  const size_t need = sol::make_layout(s).total;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  if ((size_t)dev >= g_ws.size()) g_ws.resize(dev + 1);
+  OwnedWorkspace& w = g_ws[dev];
+  if (w.bytes < need) {
+    if (w.ptr) {
+      // the previous workspace may still be read by queued work on any stream
+      if ((e = hipDeviceSynchronize()) != hipSuccess) return device_fail(e, "hipDeviceSynchronize");
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    if (hipMalloc(&w.ptr, need) != hipSuccess) {
+      w.ptr = nullptr;
+      (void)hipGetLastError();
+      return fail(SOL_ERR_NOMEM, "could not allocate a %zu-byte workspace", need);
+    }
+    w.bytes = need;
+  }
+  if ((st = summaries_checked(s, k, v, flags, w.ptr, nullptr)) != SOL_OK) return st;
+  if ((st = fused_checked(s, q, k, v, out, beta, flags, w.ptr, nullptr, nullptr)) != SOL_OK) return st;
+  return finish(flags, nullptr);
+}
+
+}  // extern "C"

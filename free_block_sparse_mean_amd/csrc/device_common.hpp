@@ -1,0 +1,51 @@
+// Small device-side helpers shared by the HIP kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sol {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 16-byte vector of the input dtype and its widening to float
+template <typename T> struct Vec16;
+template <> struct Vec16<__bf16> {
+  static constexpr int kN = 8;
+  typedef uint4 raw;
+  __device__ static inline void to_float(const raw& r, float* f) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Vec16<float> {
+  static constexpr int kN = 4;
+  typedef float4 raw;
+  __device__ static inline void to_float(const raw& r, float* f) {
+    f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w;
+  }
+};
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// float -> bfloat16, round to nearest even (finite inputs)
+__device__ inline __bf16 to_bf16(float f) { return (__bf16)f; }
+
+}  // namespace sol

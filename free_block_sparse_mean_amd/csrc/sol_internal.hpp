@@ -1,0 +1,66 @@
+// Internal interface between the C-ABI host runtime (api.cpp) and the HIP
+// kernels (prepass.hip, fused.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sol {
+
+constexpr int kBlock = 64;          // tokens per block
+constexpr int kMaxBlocks = 4096;    // n_b limit (N <= 262144), bounded by the fused kernel's LDS
+constexpr int kCovChunk = 128;      // key blocks per covariance partial
+
+enum class Dtype { BF16, F32 };
+
+// beta handling without forming beta * sigma for infinite beta
+enum BetaMode : int { kBetaFinite = 0, kBetaMinusInf = 1, kBetaPlusInf = 2 };
+
+struct Shape {
+  int B, H, N, d;
+  int n_b;      // N / 64
+  int n_b_pad;  // n_b rounded up to a multiple of 4 (row pitch of kbar_t)
+  int n_words;  // ceil(n_b / 64): mask words per query block
+  int cov_parts;  // ceil(n_b / kCovChunk)
+  long long BH() const { return (long long)B * H; }
+};
+
+struct Workspace {
+  float* kbar_t;    // [BH][d][n_b_pad]
+  float* kbar;      // [BH][n_b][d]
+  float* vsum;      // [BH][n_b][d]
+  float* kmean;     // [BH][d]
+  float* kcov;      // [BH][d][d]
+  double* kmean64;  // [BH][d]            (pre-pass scratch)
+  double* cov_part; // [BH][cov_parts][d][d] (pre-pass scratch)
+};
+
+struct Layout {
+  size_t kbar_t, kbar, vsum, kmean, kcov, kmean64, cov_part, total;
+};
+
+Layout make_layout(const Shape& s);
+Workspace bind_workspace(const Shape& s, void* base);
+
+struct FusedArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  Workspace ws;
+  float beta;
+  int beta_mode;
+  bool correction;
+  int32_t* kept_per_row;
+  uint64_t* mask_bits;
+  float* tau;
+};
+
+// Each returns the first HIP error of its launches (hipSuccess otherwise).
+hipError_t launch_prepass(const Shape& s, Dtype dt, const void* k, const void* v,
+                          const Workspace& ws, hipStream_t stream);
+hipError_t launch_fused(const Shape& s, Dtype dt, const FusedArgs& a, hipStream_t stream);
+int fused_lds_bytes(Dtype dt, int d, int n_b);
+
+}  // namespace sol

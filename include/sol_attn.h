@@ -1,0 +1,151 @@
+/*
+ * sol_attn.h - C ABI of the Sol-Attn forward library for AMD MI355X (gfx950).
+ *
+ * What it computes (per batch b, head h, 64-token query block i):
+ *   q_bar_i, k_bar_j, v_bar_j : means over each block of 64 tokens;
+ *   s_hat_ij = q_bar_i . k_bar_j / sqrt(d)            (block proxy score);
+ *   tau_i    = mu_i + beta * sigma_i, with mu_i and sigma_i the mean and
+ *              population std of row i of s_hat, obtained in closed form from
+ *              the mean m and the centred covariance C of the key summaries:
+ *              mu_i = q_bar_i.m / sqrt(d), sigma_i^2 = q_bar_i^T C q_bar_i / d;
+ *   S_i      = { j : s_hat_ij > tau_i } (strict);
+ *   out_r    = softmax attention of query row r over the tokens of the blocks
+ *              in S_i, plus (with SOL_CORRECTION) every block j outside S_i
+ *              entered as 64 virtual tokens of logit s_hat_ij and value v_bar_j.
+ * Sources: page "Sol-Attn: l'attenzione sparsa che sceglie al volo, per
+ * generare video piu in fretta" (paithon.it), sections "Perche l'attenzione
+ * pesa tanto nei video" (64-token blocks, mean-pooled proxy), "Una soglia per
+ * ogni riga" (threshold equation; closed-form mu/sigma from the key-summary
+ * mean and d x d second moments) and "Scegliere mentre si calcola" (in-pass
+ * test against tau_i; excluded blocks reused as zeroth-order terms in the
+ * same online-softmax state); the paper abstract (routing, sparse compute and
+ * correction in one online-softmax pass). The 1/sqrt(d) proxy scale and the
+ * exact virtual-token form are this library's reading of those passages.
+ *
+ * Tensor layout: q, k, v, out are contiguous [B][H][N][d] arrays in device
+ * memory, all of one dtype (bfloat16 by default, float32 with SOL_F32).
+ * N must be a multiple of 64 (no partial block), 64 <= N <= 262144, and
+ * d must be 64 or 128. Softmax scale is 1/sqrt(d).
+ *
+ * Ownership: every pointer is owned by the caller. The library keeps no
+ * pointer after a call returns. Calls are asynchronous on the given HIP stream
+ * (NULL = the null stream): buffers must stay alive until that stream has
+ * finished the work. Nothing here allocates device memory except
+ * sol_attn_fwd, which keeps one library-owned workspace per device.
+ *
+ * Errors: every entry point returns a sol_status and never aborts or throws.
+ * Arguments are validated before any device call; on failure nothing has been
+ * enqueued. sol_last_error() gives a message for the last failing call on the
+ * calling thread.
+ */
+#ifndef SOL_ATTN_H
+#define SOL_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SOL_ATTN_ABI_VERSION 1
+
+typedef enum sol_status {
+  SOL_OK = 0,
+  SOL_ERR_INVALID_ARG = 1,   /* null pointer, size <= 0, N % 64 != 0, beta NaN, bad flags */
+  SOL_ERR_UNSUPPORTED = 2,   /* d not in {64, 128}, N beyond the supported maximum       */
+  SOL_ERR_DEVICE = 3,        /* a HIP call failed (message names it)                     */
+  SOL_ERR_NOMEM = 4,         /* the library-owned workspace could not be allocated       */
+  SOL_ERR_WORKSPACE = 5      /* caller workspace NULL or smaller than required           */
+} sol_status;
+
+/* flags (bitwise or) */
+#define SOL_BF16       0x0u  /* q, k, v, out are bfloat16 (default)                         */
+#define SOL_F32        0x1u  /* q, k, v, out are float32                                    */
+#define SOL_CORRECTION 0x2u  /* fold every unselected block in as 64 virtual tokens         */
+#define SOL_DENSE      0x4u  /* keep every block (same selection as beta = -INFINITY)       */
+#define SOL_SYNC       0x8u  /* synchronise the stream before returning, report its errors  */
+#define SOL_FLAGS_ALL  0xFu
+
+/* Optional per-call outputs, all device pointers owned by the caller, each may be NULL.
+ * n_b = N / 64, W = ceil(n_b / 64).
+ *   kept_per_row [B*H*n_b]      int32: |S_i| for each query block (row of blocks)
+ *   mask_bits    [B*H*n_b*W]    uint64: bit (j % 64) of word j / 64 is set iff j in S_i
+ *   tau          [B*H*n_b]      float: tau_i as used by the selection (-inf / +inf allowed) */
+typedef struct sol_debug {
+  int32_t*  kept_per_row;
+  uint64_t* mask_bits;
+  float*    tau;
+} sol_debug;
+
+/* Byte offsets, inside a workspace, of the arrays the block-summary pre-pass
+ * writes (all float32 unless noted; BH = B*H; nbp = n_b rounded up to 4):
+ *   kbar_t  [BH][d][nbp]  block-mean keys, transposed (k_bar_j[c] at [c][j])
+ *   kbar    [BH][n_b][d]  block-mean keys
+ *   vsum    [BH][n_b][d]  block sums of values (= 64 * v_bar_j)
+ *   kmean   [BH][d]       m = mean over j of k_bar_j
+ *   kcov    [BH][d][d]    C = (1/n_b) sum_j (k_bar_j - m)(k_bar_j - m)^T
+ * the remaining bytes are scratch of the pre-pass. */
+typedef struct sol_workspace_layout {
+  size_t total_bytes;
+  size_t kbar_t;
+  size_t kbar;
+  size_t vsum;
+  size_t kmean;
+  size_t kcov;
+  size_t scratch;
+} sol_workspace_layout;
+
+/* ABI version of the loaded library (SOL_ATTN_ABI_VERSION it was built with). */
+int sol_abi_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * Valid until the next library call on the same thread. */
+const char* sol_last_error(void);
+
+/* Workspace size in bytes for a problem, 0 if the shape is invalid or unsupported. */
+size_t sol_attn_workspace_bytes(int B, int H, int N, int d);
+
+/* Offsets of the pre-pass arrays inside the workspace (see sol_workspace_layout). */
+sol_status sol_attn_workspace_layout(int B, int H, int N, int d, sol_workspace_layout* layout);
+
+/* Block-summary pre-pass: reads k and v once and writes k_bar, v sums, m and C
+ * into `workspace` (layout above). Source of m and C: page "Sol-Attn:
+ * l'attenzione sparsa che sceglie al volo" (paithon.it), section "Una soglia
+ * per ogni riga", last paragraph (mean of the compressed keys and their d x d
+ * second-moment matrix). flags: SOL_F32 selects the dtype; other bits ignored.
+ * workspace: device memory of at least sol_attn_workspace_bytes bytes. */
+sol_status sol_block_summaries(const void* k, const void* v, int B, int H, int N, int d,
+                               unsigned flags, void* workspace, size_t ws_bytes,
+                               void* hip_stream);
+
+/* Fused pass: per query block, closed-form tau_i, in-pass proxy test of every
+ * key block, exact attention on the kept blocks and (SOL_CORRECTION) the
+ * virtual-token fold of the others, in one online-softmax state; writes out.
+ * Source: same page, section "Scegliere mentre si calcola". `workspace` must
+ * hold the pre-pass results of the same k, v and shape (it is only read).
+ * dbg may be NULL. beta = -INFINITY or SOL_DENSE keeps every block;
+ * beta = +INFINITY keeps none. */
+sol_status sol_attn_fused(const void* q, const void* k, const void* v, void* out,
+                          int B, int H, int N, int d, float beta, unsigned flags,
+                          const void* workspace, size_t ws_bytes, const sol_debug* dbg,
+                          void* hip_stream);
+
+/* Whole forward on a caller stream with a caller workspace:
+ * sol_block_summaries followed by sol_attn_fused. Reentrant. */
+sol_status sol_attn_fwd_ex(const void* q, const void* k, const void* v, void* out,
+                           int B, int H, int N, int d, float beta, unsigned flags,
+                           void* hip_stream, void* workspace, size_t ws_bytes,
+                           const sol_debug* dbg);
+
+/* Whole forward on the null stream of the current device with a library-owned
+ * workspace (allocated on first use, grown when needed, held until the
+ * process ends; calls are serialised by a mutex). */
+sol_status sol_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                        int B, int H, int N, int d, float beta, unsigned flags);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOL_ATTN_H */

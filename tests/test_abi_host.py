@@ -1,0 +1,91 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/sol_attn.h declares, and rejects invalid arguments before any
+device call."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sol_attn.h")
+LIB = os.path.join(ROOT, "free_block_sparse_mean_amd", "libsolattn.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sol_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libsolattn.so is not built (run __graft_entry__.build())")
+    from free_block_sparse_mean_amd import binding
+    return binding.load_library(LIB)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert "sol_attn_fwd" in names and "sol_attn_fused" in names and len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in sol_attn.h but not exported"
+
+
+def test_abi_version(lib):
+    text = open(HEADER).read()
+    want = int(re.search(r"#define SOL_ATTN_ABI_VERSION (\d+)", text).group(1))
+    assert lib.sol_abi_version() == want
+
+
+def test_workspace_bytes(lib):
+    n = lib.sol_attn_workspace_bytes(1, 24, 131072, 128)
+    nb = 2048
+    assert n >= 24 * (3 * nb * 128 * 4 + 128 * 4 + 128 * 128 * 4)
+    assert n < 256 * 2 ** 20
+    assert lib.sol_attn_workspace_bytes(1, 1, 100, 64) == 0      # not a multiple of 64
+    assert lib.sol_attn_workspace_bytes(1, 1, 4096, 96) == 0     # unsupported d
+    assert lib.sol_attn_workspace_bytes(0, 1, 4096, 64) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 1, 4096, 64, 1.0, 0), 1),              # null pointers
+    ((1, 1, 100, 64, 1.0, 0), 1),               # N % 64
+    ((1, 1, 4096, 96, 1.0, 0), 2),              # d unsupported
+    ((0, 1, 4096, 64, 1.0, 0), 1),              # B <= 0
+    ((1, 1, 64 * 5000, 64, 1.0, 0), 2),         # N beyond the maximum
+])
+def test_invalid_arguments_fwd(lib, args, code):
+    B, H, N, d, beta, flags = args
+    st = lib.sol_attn_fwd(None, None, None, None, B, H, N, d, beta, flags)
+    assert st == code
+    assert lib.sol_last_error().decode()
+
+
+def test_invalid_beta_and_flags(lib):
+    p = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    assert lib.sol_attn_fwd(p, p, p, p, 1, 1, 4096, 64, math.nan, 0) == 1
+    assert "NaN" in lib.sol_last_error().decode()
+    assert lib.sol_attn_fwd(p, p, p, p, 1, 1, 4096, 64, 1.0, 0x100) == 1
+    assert "flag" in lib.sol_last_error().decode()
+
+
+def test_workspace_too_small(lib):
+    p = ctypes.c_void_p(16)
+    st = lib.sol_attn_fwd_ex(p, p, p, p, 1, 1, 4096, 64, 1.0, 0, None, p, 10, None)
+    assert st == 5
+    assert "workspace" in lib.sol_last_error().decode()
+    st = lib.sol_block_summaries(p, p, 1, 1, 4096, 64, 0, None, 0, None)
+    assert st == 5
+
+
+def test_layout_offsets(lib):
+    from free_block_sparse_mean_amd import binding
+    lay = binding.sol_workspace_layout()
+    assert lib.sol_attn_workspace_layout(2, 3, 64 * 100, 128, ctypes.byref(lay)) == 0
+    offs = [lay.kbar_t, lay.kbar, lay.vsum, lay.kmean, lay.kcov, lay.scratch]
+    assert offs == sorted(offs) and offs[0] == 0 and lay.total_bytes > lay.scratch
+    assert all(o % 256 == 0 for o in offs)
+    assert lay.kbar - lay.kbar_t >= 6 * 128 * 100 * 4

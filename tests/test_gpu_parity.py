@@ -1,0 +1,155 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bar: selection masks bit-exact except ties within 1e-4 of tau_i; outputs
+within rel-L2 1e-2 and max-abs 2e-2 for bf16 inputs (1e-5 / 1e-4 for float32).
+Small problems are compared on every row; they span several 64-block ballot
+words, ragged tails (n_b not a multiple of 64 or 4) and both head dims.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from free_block_sparse_mean_amd import workloads as wl
+from tests import parity_utils as pu
+
+pytestmark = pytest.mark.gpu
+
+BF, F32 = "bf16", "f32"
+
+
+def _case(w, beta, correction, gpu_lib, flags_extra=0, label=""):
+    q, k, v = wl.make_qkv(w)
+    dev = torch.device("cuda")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    flags = (gpu_lib.SOL_CORRECTION if correction else 0) | flags_extra
+    r = pu.run_gpu(qd, kd, vd, beta, flags, gpu_lib)
+    eff_beta = -math.inf if flags_extra & gpu_lib.SOL_DENSE else beta
+    nb = w.n_blocks
+    # stats are consistent with the mask
+    assert torch.equal(r["kept"], r["mask"].sum(-1).to(torch.int32))
+    assert torch.isfinite(r["out"]).all()
+    stats = []
+    for b in range(w.B):
+        for h in range(w.H):
+            stats.append(pu.check_head(q[b, h], k[b, h], v[b, h], r["out"][b, h].numpy(),
+                                       r["mask"][b, h].numpy(), r["tau"][b, h].numpy(),
+                                       eff_beta, correction, w.dtype,
+                                       label=f"{label or w.name} b{b} h{h} beta={beta}"))
+    return r, stats
+
+
+SMALL = [
+    wl.Workload("c1_small_f32", 1, 1, 4096, 64, F32, "centroid"),
+    wl.small("ragged_d128", 2, 3, 64 * 100, 128, grid=(4, 25, 64)),
+    wl.small("ragged_d64", 1, 2, 64 * 70, 64, grid=(2, 35, 64)),
+    wl.Workload("centroid_bf16", 1, 2, 64 * 90, 128, BF, "centroid"),
+    wl.small("rotated", 1, 2, 64 * 80, 128, grid=(2, 40, 64), rotate=True),
+    wl.small("skewed", 1, 2, 64 * 130, 128, grid=(2, 65, 64), skewed=True),
+    wl.small("f32_d128", 1, 2, 64 * 40, 128, dtype=F32, grid=(2, 20, 64)),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("beta", [-0.5, 0.5, 1.0, 2.0])
+@pytest.mark.parametrize("correction", [True, False], ids=["corr", "nocorr"])
+def test_small_parity(w, beta, correction, gpu_lib):
+    print(f"case {w.name} beta={beta} corr={correction}", flush=True)
+    _case(w, beta, correction, gpu_lib)
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[1], SMALL[2]], ids=lambda w: w.name)
+@pytest.mark.parametrize("correction", [True, False], ids=["corr", "nocorr"])
+def test_dense_limit(w, correction, gpu_lib):
+    """beta = -inf and the SOL_DENSE flag both keep every block: dense attention."""
+    print(f"case dense {w.name} corr={correction}", flush=True)
+    r1, _ = _case(w, -math.inf, correction, gpu_lib)
+    assert r1["mask"].all()
+    r2, _ = _case(w, 1.0, correction, gpu_lib, flags_extra=gpu_lib.SOL_DENSE)
+    assert torch.equal(r1["out"], r2["out"])
+    # and against the textbook dense routine directly
+    q, k, v = wl.make_qkv(w)
+    from oracle import sol_oracle as orc
+    for b in range(w.B):
+        ref = orc.dense_attention(q[b, 0].float().numpy(), k[b, 0].float().numpy(), v[b, 0].float().numpy())
+        got = r1["out"][b, 0].numpy()
+        tol = (pu.BF16_REL_L2, pu.BF16_MAX_ABS) if w.dtype == BF else (pu.F32_REL_L2, pu.F32_MAX_ABS)
+        assert pu.rel_l2(got, ref) <= tol[0] and np.abs(got - ref).max() <= tol[1]
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[1]], ids=lambda w: w.name)
+@pytest.mark.parametrize("correction", [True, False], ids=["corr", "nocorr"])
+def test_keep_none(w, correction, gpu_lib):
+    """beta = +inf keeps no block: pooled attention with the correction, zeros without."""
+    print(f"case keep-none {w.name} corr={correction}", flush=True)
+    r, _ = _case(w, math.inf, correction, gpu_lib)
+    assert not r["mask"].any()
+    assert (r["kept"] == 0).all()
+    if not correction:
+        assert not r["out"].any()
+
+
+@pytest.mark.parametrize("N", [64, 128, 192, 64 * 65])
+@pytest.mark.parametrize("d", [64, 128])
+def test_tiny_and_word_edges(N, d, gpu_lib):
+    """n_b = 1, 2, 3 and 65 (one block past a full 64-block mask word)."""
+    w = wl.small(f"edge_{N}_{d}", 1, 2, N, d, grid=(1, N // 64, 64))
+    for beta in (0.0, 1.0):
+        for corr in (True, False):
+            print(f"case edge N={N} d={d} beta={beta} corr={corr}", flush=True)
+            _case(w, beta, corr, gpu_lib)
+
+
+def test_identical_keys_sigma_zero(gpu_lib):
+    """All key blocks equal: sigma_i = 0, every score ties with tau; the GPU may take
+    either side, and its output must match the oracle run on its own mask."""
+    torch.manual_seed(0)
+    B, H, N, d = 1, 1, 64 * 20, 128
+    q = torch.randn(B, H, N, d).to(torch.bfloat16)
+    k = torch.randn(1, 1, 64, d).repeat(1, 1, N // 64, 1).to(torch.bfloat16)
+    v = torch.randn(B, H, N, d).to(torch.bfloat16)
+    dev = torch.device("cuda")
+    for corr in (True, False):
+        r = pu.run_gpu(q.to(dev), k.to(dev), v.to(dev), 0.5, gpu_lib.SOL_CORRECTION if corr else 0, gpu_lib)
+        pu.check_head(q[0, 0], k[0, 0], v[0, 0], r["out"][0, 0].numpy(), r["mask"][0, 0].numpy(),
+                      r["tau"][0, 0].numpy(), 0.5, corr, BF, label=f"identical keys corr={corr}")
+
+
+def test_deterministic_and_stream(gpu_lib):
+    """Two calls give bit-identical results, on a side stream and through sol_attn_fwd."""
+    w = SMALL[1]
+    q, k, v = (t.cuda() for t in wl.make_qkv(w))
+    flags = gpu_lib.SOL_CORRECTION
+    a = pu.run_gpu(q, k, v, 1.0, flags, gpu_lib)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = pu.run_gpu(q, k, v, 1.0, flags, gpu_lib, stream=s)
+    assert torch.equal(a["out"], b["out"]) and torch.equal(a["mask"], b["mask"])
+    out = torch.empty_like(q)
+    gpu_lib.sol_attn_fwd(q, k, v, out, 1.0, flags)
+    torch.cuda.synchronize()
+    assert torch.equal(out.float().cpu(), a["out"])
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[1], SMALL[2]], ids=lambda w: w.name)
+def test_prepass_summaries(w, gpu_lib):
+    """k_bar, v sums, m and C of the pre-pass against the oracle's float64 block means."""
+    from oracle import sol_oracle as orc
+    q, k, v = wl.make_qkv(w)
+    kd, vd = k.cuda(), v.cuda()
+    ws = gpu_lib.new_workspace(w.B, w.H, w.N, w.d)
+    gpu_lib.sol_block_summaries(kd, vd, ws)
+    torch.cuda.synchronize()
+    views = {n: t.cpu().double().numpy() for n, t in gpu_lib.workspace_views(ws, w.B, w.H, w.N, w.d).items()}
+    for b in range(w.B):
+        for h in range(w.H):
+            kbar = orc.block_means(k[b, h].float().numpy())
+            vbar = orc.block_means(v[b, h].float().numpy())
+            m, C = orc.key_summary_moments(kbar)
+            sc = np.abs(kbar).max()
+            np.testing.assert_allclose(views["kbar"][b, h], kbar, rtol=0, atol=1e-6 * sc)
+            np.testing.assert_allclose(views["kbar_t"][b, h], kbar.T, rtol=0, atol=1e-6 * sc)
+            np.testing.assert_allclose(views["vsum"][b, h], 64 * vbar, rtol=0, atol=64e-6 * np.abs(vbar).max())
+            np.testing.assert_allclose(views["kmean"][b, h], m, rtol=0, atol=1e-6 * sc)
+            np.testing.assert_allclose(views["kcov"][b, h], C, rtol=0, atol=1e-5 * np.abs(C).max())

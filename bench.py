@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the Sol-Attn forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+the block-summary pre-pass (sol_block_summaries) followed by the fused
+route + exact sparse attention + correction pass (sol_attn_fused), the same
+work as one sol_attn_fwd_ex call. Inputs are resident in HBM before the timed
+region starts.
+
+Workload (default): B=1, H=24, N=131072 (2048 blocks of 64), d=128, bf16,
+synthetic video-latent field on a 32x64x64 grid; headline beta=1.5 with the
+correction; beta=2.0 and the dense path (every block kept) are timed too.
+
+Prints ONE JSON line. `value` is dense-equivalent TFLOP/s of the headline
+step (4*B*H*N^2*d / step time); per-beta ms and TFLOP/s are in `per_beta`.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "sparse-attn fwd ms + dense-equiv TFLOP/s at seq 128K, H24 d128 bf16, per β"
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "fused_c4_pmc.json")
+FUSED_SRC = os.path.join(ROOT, "free_block_sparse_mean_amd", "csrc", "fused.hip")
+
+
+def dense_equiv_flop(w) -> float:
+    return 4.0 * w.B * w.H * float(w.N) ** 2 * w.d
+
+
+def kept_flop(w, kept_blocks: int) -> float:
+    """MFMA work the method must do: 4 * 64 * 64 * d per kept (query block, key block) tile."""
+    return 4.0 * 64 * 64 * w.d * kept_blocks
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per fused launch from the committed rocprofv3 counter summary, or None
+    if there is none or the fused kernel source changed since it was taken."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    s = json.load(open(PMC_SUMMARY))
+    if s.get("fused_src_sha256_16") != source_hash(FUSED_SRC):
+        return None
+    return s.get("hbm_bytes_per_launch")
+
+
+def time_steps(fn_pre, fn_fused, steps: int):
+    """Time `steps` steps on the current stream; returns (ms/step, fused ms, prepass ms, wall s)."""
+    import torch
+    st = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    e0, e1 = ev(), ev()
+    pa, pb, fa, fb = ([ev() for _ in range(steps)] for _ in range(4))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(st)
+    for i in range(steps):
+        pa[i].record(st)
+        fn_pre()
+        pb[i].record(st)
+        fa[i].record(st)
+        fn_fused()
+        fb[i].record(st)
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    fused = sum(fa[i].elapsed_time(fb[i]) for i in range(steps)) / steps
+    pre = sum(pa[i].elapsed_time(pb[i]) for i in range(steps)) / steps
+    return ms, fused, pre, wall
+
+
+def cpu_baseline(w, q, k, v, beta: float, blocks_per_head: int, heads):
+    """The oracle, untuned, on a bounded sample: `blocks_per_head` seeded query blocks of
+    each listed head. Returns the dense-equivalent TFLOP/s of the sampled rows."""
+    import numpy as np
+    from oracle import sol_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    rng = np.random.default_rng(1234)
+    nb = w.N // 64
+    per_block = 4.0 * 64 * w.N * w.d
+    arrays = [(q[0, h].float().numpy(), k[0, h].float().numpy(), v[0, h].float().numpy()) for h in heads]
+    picks = [np.sort(rng.choice(nb, size=blocks_per_head, replace=False)) for _ in heads]
+    t0 = time.perf_counter()
+    for (qh, kh, vh), qb in zip(arrays, picks):
+        orc.sol_attention_head(qh, kh, vh, beta, True, query_blocks=qb)
+    el = time.perf_counter() - t0
+    n_blocks = blocks_per_head * len(heads)
+    tflops = n_blocks * per_block / el / 1e12
+    return {
+        "value": tflops, "unit": "TFLOP/s (dense-equivalent)", "cores": int(cores), "kind": "oracle",
+        "sample": (f"{blocks_per_head} seeded query blocks x {len(heads)} heads of the "
+                   f"{w.name} workload (B={w.B}, H={w.H}, N={w.N}, d={w.d}), beta={beta}, "
+                   f"correction on: {n_blocks} of {w.B * w.H * nb} query blocks"),
+        "seconds": el,
+        "extrapolated_full_s": el * (w.B * w.H * nb) / n_blocks,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4_stress_128k")
+    ap.add_argument("--beta", type=float, default=1.5, help="headline beta")
+    ap.add_argument("--extra-betas", default="2.0", help="comma list, '' for none")
+    ap.add_argument("--no-dense", action="store_true", help="skip timing the dense path")
+    ap.add_argument("--no-correction", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-blocks-per-head", type=int, default=8)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy 5 times (for counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 2
+
+    if args.copy_calibration:
+        n = 512 * 2 ** 20
+        x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return 0
+
+    from free_block_sparse_mean_amd import binding as sb, workloads as wl
+
+    w = wl.CONFIGS[args.workload]
+    t_gen = time.perf_counter()
+    q, k, v = wl.make_qkv(w)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(qd)
+    ws = sb.new_workspace(w.B, w.H, w.N, w.d, dev)
+    nb = w.n_blocks
+    kept = torch.zeros((w.B, w.H, nb), dtype=torch.int32, device=dev)
+    corr = 0 if args.no_correction else sb.SOL_CORRECTION
+    torch.cuda.synchronize()
+
+    def stepper(beta, flags):
+        pre = lambda: sb.sol_block_summaries(kd, vd, ws)
+        fused = lambda: sb.sol_attn_fused(qd, kd, vd, out, beta, flags, ws)
+        return pre, fused
+
+    def measure(beta, flags, steps, warmup):
+        # untimed call with stats: kept blocks (the algorithmic work) of this setting
+        sb.sol_block_summaries(kd, vd, ws)
+        sb.sol_attn_fused(qd, kd, vd, out, beta, flags, ws, kept_per_row=kept)
+        torch.cuda.synchronize()
+        n_kept = int(kept.sum().item())
+        pre, fused = stepper(beta, flags)
+        for _ in range(warmup):
+            pre(); fused()
+        ms, fused_ms, pre_ms, wall = time_steps(pre, fused, steps)
+        kf = kept_flop(w, n_kept)
+        return {
+            "beta": beta if math.isfinite(beta) else str(beta),
+            "ms": ms, "fused_ms": fused_ms, "prepass_ms": pre_ms, "wall_s": wall,
+            "dense_equiv_tflops": dense_equiv_flop(w) / (ms * 1e-3) / 1e12,
+            "density": n_kept / (w.B * w.H * nb * nb),
+            "kept_blocks": n_kept,
+            "kept_tflops_fused": kf / (fused_ms * 1e-3) / 1e12,
+            "mfma_frac_fused": kf / (fused_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "prepass_hbm_gbs": 2.0 * w.B * w.H * w.N * w.d * 2 / (pre_ms * 1e-3) / 1e9,
+        }
+
+    head = measure(args.beta, corr, args.steps, args.warmup)
+    # the two-call step equals one sol_attn_fwd_ex call (bit for bit)
+    ref = out.clone()
+    sb.sol_attn_fwd_ex(qd, kd, vd, out, args.beta, corr, workspace=ws)
+    torch.cuda.synchronize()
+    same_as_fwd_ex = bool(torch.equal(ref, out))
+
+    per_beta = {str(args.beta): head}
+    small_steps = max(3, args.steps // 2)
+    for b in [float(x) for x in args.extra_betas.split(",") if x.strip()]:
+        per_beta[str(b)] = measure(b, corr, small_steps, 1)
+    if not args.no_dense:
+        dense = measure(-math.inf, corr | sb.SOL_DENSE, small_steps, 1)
+        per_beta["dense"] = dense
+        for key, r in per_beta.items():
+            if key != "dense":
+                r["speedup_vs_dense"] = dense["ms"] / r["ms"]
+
+    kf = kept_flop(w, head["kept_blocks"])
+    achieved = kf / (head["fused_ms"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": traffic_from_profile(),
+                "kernel": "fused_kernel<bf16,128,correction>",
+                "algorithmic_flop_per_launch": kf}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        heads = list(range(w.H))
+        cpu = cpu_baseline(w, q, k, v, args.beta, args.cpu_blocks_per_head, heads)
+
+    line = {
+        "metric": METRIC,
+        "value": head["dense_equiv_tflops"],
+        "unit": "TFLOP/s (dense-equivalent)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "beta": args.beta, "correction": not args.no_correction,
+                   "grid": list(w.grid) if w.grid else None},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_beta": per_beta,
+        "prepass": {"ms": head["prepass_ms"], "hbm_gbs": head["prepass_hbm_gbs"],
+                    "frac": head["prepass_hbm_gbs"] / PEAK_HBM_GBS},
+        "checks": {"two_call_step_equals_fwd_ex": same_as_fwd_ex},
+        "input_gen_s": t_gen,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -47,7 +47,7 @@ class sol_debug(ctypes.Structure):
 
 class sol_workspace_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("total_bytes", "kbar_t", "kbar", "vsum", "kmean", "kcov", "scratch")]
+                ("total_bytes", "kbar_t", "kbar", "vsum", "kmean", "kcov", "vt", "scratch")]
 
 
 _lib = None
@@ -161,6 +161,7 @@ def workspace_views(ws: torch.Tensor, B: int, H: int, N: int, d: int) -> Dict[st
         "vsum": f32(lay.vsum, (B, H, nb, d)),
         "kmean": f32(lay.kmean, (B, H, d)),
         "kcov": f32(lay.kcov, (B, H, d, d)),
+        "vt": ws[lay.vt:lay.vt + 2 * B * H * N * d].view(torch.bfloat16).view(B, H, nb, d, BLOCK),
     }
 
 

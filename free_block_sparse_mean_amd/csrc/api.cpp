@@ -25,8 +25,9 @@ Layout make_layout(const Shape& s) {
   L.vsum = off;     off += up256(bh * nb * d * 4);
   L.kmean = off;    off += up256(bh * d * 4);
   L.kcov = off;     off += up256(bh * d * d * 4);
-  L.kmean64 = off;  off += up256(bh * d * 8);
-  L.cov_part = off; off += up256(bh * (size_t)s.cov_parts * d * d * 8);
+  L.vt = off;       off += up256(bh * nb * d * 64 * 2);
+  L.s1_part = off;  off += up256(bh * (size_t)s.cov_parts * d * 8);
+  L.s2_part = off;  off += up256(bh * (size_t)s.cov_parts * d * d * 8);
   L.total = off;
   return L;
 }
@@ -40,8 +41,9 @@ Workspace bind_workspace(const Shape& s, void* base) {
   w.vsum = reinterpret_cast<float*>(b + L.vsum);
   w.kmean = reinterpret_cast<float*>(b + L.kmean);
   w.kcov = reinterpret_cast<float*>(b + L.kcov);
-  w.kmean64 = reinterpret_cast<double*>(b + L.kmean64);
-  w.cov_part = reinterpret_cast<double*>(b + L.cov_part);
+  w.vt = reinterpret_cast<__bf16*>(b + L.vt);
+  w.s1_part = reinterpret_cast<double*>(b + L.s1_part);
+  w.s2_part = reinterpret_cast<double*>(b + L.s2_part);
   return w;
 }
 
@@ -179,7 +181,8 @@ sol_status sol_attn_workspace_layout(int B, int H, int N, int d, sol_workspace_l
   layout->vsum = L.vsum;
   layout->kmean = L.kmean;
   layout->kcov = L.kcov;
-  layout->scratch = L.kmean64;
+  layout->vt = L.vt;
+  layout->scratch = L.s1_part;
   return ok();
 }
 

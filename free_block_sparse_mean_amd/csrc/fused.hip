@@ -11,31 +11,40 @@
 //     keys produces the proxy scores and tests them against tau_i as they
 //     appear; kept blocks go to an inner loop over the original K and V for
 //     exact attention; excluded blocks are reused as zeroth-order terms (the
-//     block-mean key for all its tokens) in the same softmax state.
+//     block-mean key for all their tokens) in the same softmax state.
 //
-// One workgroup (4 waves, 256 lanes) per query block i of one (b, h):
-//   1. stage Q_i (64 x d) in LDS, q_bar_i by column sums, Q operands to VGPRs;
-//   2. tau_i from q_bar_i, m and C (C read once from L2, 64 KiB at d = 128);
-//   3. outer loop over key blocks: lane-per-block proxy scores from the
-//      transposed summaries k_bar^T (coalesced rows of n_b floats); the strict
-//      test against tau_i is folded into 64-bit wave ballots, one word per 64
-//      key blocks, kept in LDS (never in HBM);
-//   4. correction accumulators for the unselected blocks: own running max c_i,
-//      weights w_j = exp(s_hat_ij - c_i), L_i = 64 sum w_j, A_i = sum w_j vsum_j;
-//   5. inner loop over the set bits: K_j and V_j^T staged in LDS, per wave 16
-//      query rows x 64 keys: S^T = K_j Q^T and O^T += V_j^T P^T with
-//      v_mfma_f32_16x16x32_bf16, online softmax in base 2 in fp32, P as bf16;
-//   6. epilogue: out = (O 2^(m-M) + A 2^(c-M)) / (l 2^(m-M) + L 2^(c-M)).
+// One workgroup (4 waves, 256 lanes) takes G consecutive query blocks of one
+// (b, h) (G <= 4, chosen so their proxy rows fit in LDS):
+//   1. q_bar for the G blocks from 16-byte loads of Q (wave shuffles + LDS);
+//   2. tau for the G blocks from q_bar, m and C (C read once from L2);
+//   3. outer loop over key blocks: lane-per-4-blocks proxy scores from the
+//      transposed summaries k_bar^T, each k_bar value loaded once for all G
+//      query blocks; the strict test against tau folded into 64-bit wave
+//      ballots, one word per 64 key blocks, kept in LDS (never in HBM);
+//   4. correction for the unselected blocks of each query block: own running
+//      max c, weights w_j = exp(s_hat_j - c), L = 64 sum w_j, A = sum w_j vsum_j,
+//      each vsum row loaded once for all G blocks;
+//   5. inner loop over the set bits of the G blocks, one flat sequence of
+//      (block, key block) tiles: the K tile and the transposed V tile of the
+//      next tile are loaded into registers while the current one is computed
+//      from LDS; per wave 16 query rows x 64 keys, S^T = K Q^T and
+//      O^T += V^T P^T on v_mfma_f32_16x16x32_bf16, online softmax in base 2
+//      in fp32, P rounded to bf16;
+//   6. per query block: out = (O 2^(m-M) + A 2^(c-M)) / (l 2^(m-M) + L 2^(c-M)).
 // Each lane owns one query row (lane % 16) of its wave and a quarter of the
-// keys / head dims (lane / 16), so row statistics need only two xor-shuffles
-// and rescaling is lane-local.
+// keys / head dims (lane / 16): row statistics need two xor-shuffles and the
+// rescale is lane-local.
+//
+// Workgroups are mapped so that consecutive work items (neighbouring query
+// blocks of one head, which keep largely the same key blocks) run on the
+// same XCD and share its L2.
 //
 // Bound: bf16 MFMA on the kept tiles (4*64*64*d flop per kept block); the
-// summary scan and the correction read n_b*d*4 bytes each per query block
-// from L2.
+// summary scan and the correction read n_b*d*4 bytes each per G query blocks.
 //
 // The float32 instantiation (small problems, tighter tolerance) keeps the same
-// routing and correction and replaces step 5 by fp32 VALU dot products.
+// routing and correction and computes the kept tiles with fp32 VALU dot
+// products from LDS-staged K and V, without prefetch.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -44,16 +53,20 @@
 namespace sol {
 namespace {
 
+constexpr int kGMax = 4;
+
 struct FusedParams {
   const void* q;
   const void* k;
   const void* v;
   void* out;
+  const __bf16* vt;
   const float* kbar_t;
   const float* vsum;
   const float* kmean;
   const float* kcov;
-  int n_b, n_b_pad, n_words;
+  int n_b, n_b_pad, n_words, G, n_groups;
+  long long items, per_xcd;
   long long N;
   float beta;
   int beta_mode;
@@ -63,435 +76,661 @@ struct FusedParams {
 };
 
 template <typename T, int D> struct Geom;
+// bf16: K tile [64][D] and V^T tile [D][64], unpadded; 16-byte chunks are
+// placed with an XOR swizzle so the MFMA operand reads hit distinct LDS banks.
+// Two buffers: the next kept tile is loaded straight into LDS
+// (global_load_lds_dwordx4) while the current one is computed.
 template <int D> struct Geom<__bf16, D> {
-  static constexpr int kKPitch = D + 8;     // elements per K (and staged Q) row
-  static constexpr int kVPitch = 64 + 8;    // elements per V^T row
-  static constexpr int kKBytes = 64 * kKPitch * 2;
-  static constexpr int kVBytes = D * kVPitch * 2;
+  static constexpr int kKBytes = 64 * D * 2;
+  static constexpr int kVBytes = D * 64 * 2;
+  static constexpr int kBufBytes = kKBytes + kVBytes;
+  static constexpr int kBuffers = 2;
 };
 template <int D> struct Geom<float, D> {
   static constexpr int kKPitch = D + 4;
   static constexpr int kVPitch = D + 4;
   static constexpr int kKBytes = 64 * kKPitch * 4;
   static constexpr int kVBytes = 64 * kVPitch * 4;
+  static constexpr int kBufBytes = kKBytes + kVBytes;
+  static constexpr int kBuffers = 1;
 };
+
+// LDS position (in 16-byte chunks) of chunk c of row r of a K tile: rows of
+// D/8 chunks; the swizzle spreads the 16 rows one MFMA operand read touches
+// over distinct banks.
+template <int D> __device__ __forceinline__ int k_pos(int r, int c) {
+  return r * (D / 8) + (c ^ (D == 128 ? (r & 15) : ((r >> 1) & 7)));
+}
+// LDS position of chunk kc (keys 8kc .. 8kc+7) of row d of a V^T tile.
+__device__ __forceinline__ int v_pos(int d, int kc) { return d * 8 + (kc ^ ((d >> 1) & 7)); }
 
 __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
 
+// LDS map. Static: two tile buffers A and B (separate objects, so the compiler
+// can see that loads into one do not alias reads of the other); during
+// routing they hold the G proxy rows (rows_per_buf rows each). Dynamic:
+// [masks | qa | acc | misc].
 template <typename T, int D> struct Lds {
-  static constexpr int kStage = Geom<T, D>::kKBytes + Geom<T, D>::kVBytes;
-  __host__ __device__ static int sh(int) { return kStage; }
-  __host__ __device__ static int masks(int n_b) { return kStage + align16(4 * n_b); }
-  __host__ __device__ static int qbar(int n_b) {
-    return masks(n_b) + align16(8 * ((n_b + 63) / 64));
-  }
-  __host__ __device__ static int acc(int n_b) { return qbar(n_b) + 4 * D; }
-  __host__ __device__ static int misc(int n_b) { return acc(n_b) + 4 * 256; }
-  __host__ __device__ static int bytes(int n_b) { return misc(n_b) + 4 * 16; }
+  static constexpr int kBuf = Geom<T, D>::kBufBytes;
+  __host__ __device__ static int rows_per_buf(int nbp) { return kBuf / (4 * nbp); }
+  __host__ __device__ static int masks() { return 0; }
+  __host__ __device__ static int qa(int G, int nw) { return align16(8 * G * nw); }
+  __host__ __device__ static int acc(int G, int nw) { return qa(G, nw) + 4 * D * kGMax; }
+  __host__ __device__ static int misc(int G, int nw) { return acc(G, nw) + 4 * 4 * D * kGMax; }
+  __host__ __device__ static int bytes(int G, int nw) { return misc(G, nw) + 4 * 64; }
 };
+// misc slots (floats)
+constexpr int kRed = 0;          // [4 waves][8] reduction scratch
+constexpr int kTot = 32;         // [8] reduction totals
+constexpr int kTau = 40;         // [kGMax]
+constexpr int kC2 = 44;          // [kGMax] correction max (base 2), -inf if none
+constexpr int kL = 48;           // [kGMax] correction denominator 64 * sum w
 
 constexpr float inv_sqrt(int d) { return d == 64 ? 0.125f : 0.08838834764831845f; }
 
-// Sum over the workgroup of one float per thread; every thread gets the total.
-__device__ inline float block_sum(float x, float* red) {
-  x = wave_sum(x);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = x;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
-}
-__device__ inline float block_max(float x, float* red) {
-  x = wave_max(x);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = x;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-
-template <typename T, int D, bool CORR>
-__global__ __launch_bounds__(256) void fused_kernel(FusedParams p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  using G = Geom<T, D>;
-  using L = Lds<T, D>;
-  constexpr float kInvSqrtD = inv_sqrt(D);
-  constexpr float kScale2 = kInvSqrtD * kLog2e;   // logit -> base-2 exponent
-
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int n_b = p.n_b;
-  const long long item = blockIdx.x;
-  const long long bh = item / n_b;
-  const int qi = (int)(item - bh * n_b);
-
-  T* stK = reinterpret_cast<T*>(lds);
-  T* stV = reinterpret_cast<T*>(lds + G::kKBytes);
-  float* sh = reinterpret_cast<float*>(lds + L::sh(n_b));
-  uint64_t* masks = reinterpret_cast<uint64_t*>(lds + L::masks(n_b));
-  float* qbar = reinterpret_cast<float*>(lds + L::qbar(n_b));
-  float* accbuf = reinterpret_cast<float*>(lds + L::acc(n_b));
-  float* misc = reinterpret_cast<float*>(lds + L::misc(n_b));
-
-  const T* Qg = static_cast<const T*>(p.q) + ((size_t)bh * p.N + (size_t)qi * kBlock) * D;
-  const T* Kg = static_cast<const T*>(p.k) + (size_t)bh * p.N * D;
-  const T* Vg = static_cast<const T*>(p.v) + (size_t)bh * p.N * D;
-
-  // ---- 1. Q tile -> LDS (K slot), q_bar, Q operands -------------------------
-  {
-    using V16 = Vec16<T>;
-    constexpr int E = V16::kN, CH = D / E;
-    for (int c = t; c < 64 * CH; c += 256) {
-      const int r = c / CH, cc = c % CH;
-      *reinterpret_cast<typename V16::raw*>(stK + r * G::kKPitch + cc * E) =
-          reinterpret_cast<const typename V16::raw*>(Qg + (size_t)r * D)[cc];
-    }
-  }
-  __syncthreads();
-  {
-    constexpr int P = 256 / D;
-    const int c = t % D, part = t / D;
-    float s = 0.f;
-    for (int r = part; r < 64; r += P) s += (float)stK[r * G::kKPitch + c];
-    accbuf[t] = s;
-  }
-  __syncthreads();
-  if (t < D) {
-    float s = 0.f;
+// Sum over the workgroup of NV floats per thread; totals land in misc[kTot + v].
+template <int NV>
+__device__ inline void block_sum_n(float (&x)[NV], float* misc) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-    for (int part = 0; part < 256 / D; ++part) s += accbuf[part * D + t];
-    qbar[t] = s * (1.0f / kBlock);
-  }
-  const int row = 16 * w + (lane & 15);   // this lane's query row within the block
-  const int grp = lane >> 4;              // this lane's quarter of keys / dims
-  constexpr int KS = D / 32;
-  bf16x8 qop[std::is_same<T, __bf16>::value ? KS : 1];
-  float qf[std::is_same<T, float>::value ? D / 4 : 1];
-  if constexpr (std::is_same<T, __bf16>::value) {
+  for (int i = 0; i < NV; ++i) x[i] = wave_sum(x[i]);
+  __syncthreads();
+  if (lane == 0)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qop[ks] = *reinterpret_cast<const bf16x8*>(stK + row * G::kKPitch + ks * 32 + grp * 8);
+    for (int i = 0; i < NV; ++i) misc[kRed + w * 8 + i] = x[i];
+  __syncthreads();
+  if (threadIdx.x < NV)
+    misc[kTot + threadIdx.x] = (misc[kRed + threadIdx.x] + misc[kRed + 8 + threadIdx.x]) +
+                               (misc[kRed + 16 + threadIdx.x] + misc[kRed + 24 + threadIdx.x]);
+  __syncthreads();
+}
+template <int NV>
+__device__ inline void block_max_n(float (&x)[NV], float* misc) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) x[i] = wave_max(x[i]);
+  __syncthreads();
+  if (lane == 0)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) misc[kRed + w * 8 + i] = x[i];
+  __syncthreads();
+  if (threadIdx.x < NV)
+    misc[kTot + threadIdx.x] = fmaxf(fmaxf(misc[kRed + threadIdx.x], misc[kRed + 8 + threadIdx.x]),
+                                     fmaxf(misc[kRed + 16 + threadIdx.x], misc[kRed + 24 + threadIdx.x]));
+  __syncthreads();
+}
+
+struct Tile {
+  int g, j;   // query block within the group, key block; g < 0 when done
+};
+
+// Next kept (g, j) strictly after `cur` in (g, j) order, from the LDS masks.
+__device__ inline Tile next_tile(Tile cur, const uint64_t* masks, int nG, int n_words) {
+  int g = cur.g, j = cur.j + 1;
+  while (g < nG) {
+    const int wi = j >> 6;
+    if (wi >= n_words) { ++g; j = 0; continue; }
+    const uint64_t word = masks[g * n_words + wi] & (~0ull << (j & 63));
+    if (word) return Tile{g, wi * 64 + (int)__builtin_ctzll(word)};
+    j = (wi + 1) * 64;
+  }
+  return Tile{-1, 0};
+}
+
+// Per-lane state of the exact phase (one query row, a quarter of its keys / dims).
+template <typename T, int D> struct ExactState {
+  static constexpr bool kBF = std::is_same<T, __bf16>::value;
+  static constexpr int KS = D / 32;                 // k-steps of 32 head dims
+  static constexpr int NACC = kBF ? D / 16 : 1;     // O^T tiles of 16 head dims
+  static constexpr int NF = kBF ? 1 : D / 4;        // fp32 path: head dims per lane
+  bf16x8 qop[kBF ? KS : 1];
+  float qf[NF];
+  f32x4 oacc[NACC];
+  float of[NF];
+  float mrow, lrow;
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void reset_block(ExactState<T, D>& st, const T* Qr, int lane) {
+  using S = ExactState<T, D>;
+  const int grp = lane >> 4;
+  st.mrow = -INFINITY;
+  st.lrow = 0.f;
+#pragma unroll
+  for (int i = 0; i < S::NACC; ++i) st.oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < S::NF; ++i) st.of[i] = 0.f;
+  if constexpr (S::kBF) {
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) st.qop[ks] = *reinterpret_cast<const bf16x8*>(Qr + ks * 32 + grp * 8);
   } else {
 #pragma unroll
-    for (int e = 0; e < D / 4; ++e) qf[e] = stK[row * G::kKPitch + grp * (D / 4) + e];
-  }
-  __syncthreads();
-
-  // ---- 2. threshold tau_i = mu_i + beta sigma_i (closed form) ---------------
-  float tau;
-  {
-    const float* C = p.kcov + (size_t)bh * D * D;
-    const float* m = p.kmean + (size_t)bh * D;
-    constexpr int P = 256 / D;
-    const int r = t % D, part = t / D;
-    float y = 0.f;
-    for (int c = part; c < D; c += P) y += C[(size_t)c * D + r] * qbar[c];
-    const float qcq = block_sum(qbar[r] * y, misc);
-    const float qm = block_sum(t < D ? qbar[t] * m[t] : 0.f, misc + 4);
-    const float mu = qm * kInvSqrtD;
-    const float sigma = sqrtf(fmaxf(qcq, 0.f) * (1.0f / D));
-    if (p.beta_mode == kBetaMinusInf) tau = -INFINITY;
-    else if (p.beta_mode == kBetaPlusInf) tau = INFINITY;
-    else tau = mu + p.beta * sigma;
-  }
-
-  // ---- 3a. outer loop: proxy scores of every key block ----------------------
-  {
-    const float* kt = p.kbar_t + (size_t)bh * D * p.n_b_pad;
-    for (int j4 = 4 * t; j4 < n_b; j4 += 1024) {
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll 16
-      for (int c = 0; c < D; ++c) {
-        const float4 kv = *reinterpret_cast<const float4*>(kt + (size_t)c * p.n_b_pad + j4);
-        const float qc = qbar[c];
-        a0 += qc * kv.x; a1 += qc * kv.y; a2 += qc * kv.z; a3 += qc * kv.w;
-      }
-      sh[j4] = a0 * kInvSqrtD;
-      if (j4 + 1 < n_b) sh[j4 + 1] = a1 * kInvSqrtD;
-      if (j4 + 2 < n_b) sh[j4 + 2] = a2 * kInvSqrtD;
-      if (j4 + 3 < n_b) sh[j4 + 3] = a3 * kInvSqrtD;
+    for (int e = 0; e < S::NF; e += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(Qr + grp * S::NF + e);
+      st.qf[e] = x.x; st.qf[e + 1] = x.y; st.qf[e + 2] = x.z; st.qf[e + 3] = x.w;
     }
   }
-  __syncthreads();
+}
 
-  // ---- 3b. strict test against tau_i -> one 64-bit word per 64 key blocks ---
-  float cmax = -INFINITY;
-  int kept = 0;
-  for (int g = w; g < p.n_words; g += 4) {
-    const int j = g * 64 + lane;
-    const bool valid = j < n_b;
-    const float s = valid ? sh[j] : 0.f;
-    const bool keep = valid && (s > tau);
-    const uint64_t word = __ballot(keep);
-    if (valid && !keep) cmax = fmaxf(cmax, s);
-    if (lane == 0) masks[g] = word;
-    kept += __popcll(word);
-  }
-  cmax = block_max(cmax, misc);
-  {
-    __syncthreads();
-    if (lane == 0) misc[8 + w] = (float)kept;
-    __syncthreads();
-    kept = (int)(misc[8] + misc[9] + misc[10] + misc[11]);
-  }
-  const long long qrow = bh * n_b + qi;
-  if (t == 0) {
-    if (p.kept_per_row) p.kept_per_row[qrow] = kept;
-    if (p.tau_out) p.tau_out[qrow] = tau;
-  }
-  if (p.mask_bits)
-    for (int g = t; g < p.n_words; g += 256) p.mask_bits[qrow * p.n_words + g] = masks[g];
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+typedef __attribute__((address_space(1))) const void gbl_ptr_t;
 
-  // ---- 4. correction: unselected blocks as 64 virtual tokens ---------------
-  float c2 = -INFINITY, Lsum = 0.f;
-  if constexpr (CORR) {
-    if (cmax > -INFINITY) {
-      c2 = cmax * kLog2e;
-      float part_l = 0.f;
-      for (int j = t; j < n_b; j += 256) {
-        const bool keep = (masks[j >> 6] >> (j & 63)) & 1ull;
-        const float wj = keep ? 0.f : exp2f(sh[j] * kLog2e - c2);
-        sh[j] = wj;
-        part_l += wj;
+// bf16: start loading the K tile and the transposed V tile of key block j
+// straight into LDS buffer `buf` (each lane moves D/32 chunks of each).
+// Completion is awaited with s_waitcnt vmcnt(0) before the next barrier.
+template <int D>
+__device__ __forceinline__ void issue_tile(unsigned char* buf, const __bf16* Kh, const __bf16* Vt,
+                                           long long bh, int n_b, int j, int t) {
+  constexpr int NI = D / 32;   // instructions per lane for each of K and V^T
+  const __bf16* Kj = Kh + (size_t)j * kBlock * D;
+  const __bf16* Vj = Vt + ((size_t)bh * n_b + j) * D * 64;
+  const int wbase = t & ~63;   // first chunk of this wave in each 256-chunk slab
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int q = i * 256 + t;                  // LDS chunk this lane fills
+    const int r = q / (D / 8), pc = q % (D / 8);
+    const int c = pc ^ (D == 128 ? (r & 15) : ((r >> 1) & 7));
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(Kj + r * D + c * 8),
+                                     (lds_ptr_t*)(buf + (i * 256 + wbase) * 16), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int q = i * 256 + t;
+    const int d = q >> 3, pc = q & 7;
+    const int kc = pc ^ ((d >> 1) & 7);
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(Vj + d * 64 + kc * 8),
+                                     (lds_ptr_t*)(buf + Geom<__bf16, D>::kKBytes + (i * 256 + wbase) * 16),
+                                     16, 0, 0);
+  }
+}
+
+// fp32: stage the K and V tiles of key block j in LDS (synchronously)
+template <int D>
+__device__ __forceinline__ void commit_f32(float* stK, float* stV, const float* Kh, const float* Vh,
+                                           int j, int t) {
+  using Gm = Geom<float, D>;
+  const float* Kj = Kh + (size_t)j * kBlock * D;
+  const float* Vj = Vh + (size_t)j * kBlock * D;
+  constexpr int CH = D / 4;
+  for (int c = t; c < 64 * CH; c += 256) {
+    const int r = c / CH, cc = c % CH;
+    *reinterpret_cast<float4*>(stK + r * Gm::kKPitch + cc * 4) =
+        reinterpret_cast<const float4*>(Kj + (size_t)r * D)[cc];
+    *reinterpret_cast<float4*>(stV + r * Gm::kVPitch + cc * 4) =
+        reinterpret_cast<const float4*>(Vj + (size_t)r * D)[cc];
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void compute_tile(ExactState<T, D>& st, const unsigned char* buf, int lane) {
+  using S = ExactState<T, D>;
+  using Gm = Geom<T, D>;
+  constexpr float kScale2 = inv_sqrt(D) * kLog2e;   // logit -> base-2 exponent
+  const int grp = lane >> 4;
+  if constexpr (S::kBF) {
+    const unsigned char* bK = buf;
+    const unsigned char* bV = buf + Gm::kKBytes;
+    // S^T (64 keys x 16 queries of this wave): 4 key tiles of 16
+    f32x4 s[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            bK + 16 * k_pos<D>(kt * 16 + (lane & 15), ks * 4 + grp));
+        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, st.qop[ks], s[kt], 0, 0, 0);
       }
-      Lsum = block_sum(part_l, misc) * (float)kBlock;   // syncs: sh is complete
-      constexpr int P = 256 / D;
-      const int col = t % D, part = t / D;
-      const float* vs = p.vsum + (size_t)bh * n_b * D + col;
+    }
+    // online softmax (base 2): lane holds keys kt*16 + grp*4 + i of its query row
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[kt][i]);
+    tmax *= kScale2;
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = fmaxf(st.mrow, tmax);
+    const float alpha = exp2f(st.mrow - mnew);
+    float psum = 0.f;
+    bf16x8 pop[2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pvv = exp2f(s[kt][i] * kScale2 - mnew);
+        psum += pvv;
+        pop[kt >> 1][(kt & 1) * 4 + i] = to_bf16(pvv);
+      }
+    st.lrow = st.lrow * alpha + psum;
+    st.mrow = mnew;
+#pragma unroll
+    for (int dt = 0; dt < S::NACC; ++dt) st.oacc[dt] *= alpha;
+    // O^T (d x 16 queries) += V^T (d x 64 keys) P^T: two k-steps of 32 keys
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int dt = 0; dt < S::NACC; ++dt) {
+        const int d = dt * 16 + (lane & 15);
+        const int kc = ks * 4 + (grp >> 1), off = (grp & 1) * 8;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(bV + 16 * v_pos(d, kc) + off);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(bV + 16 * v_pos(d, kc + 2) + off);
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        st.oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[ks], st.oacc[dt], 0, 0, 0);
+      }
+    }
+  } else {
+    const float* stK = reinterpret_cast<const float*>(buf);
+    const float* stV = reinterpret_cast<const float*>(buf + Gm::kKBytes);
+    // fp32: 4 lanes per query row, each a quarter of the head dims
+    float sv[64];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int key = 0; key < 64; ++key) {
+      const float* kr = stK + key * Gm::kKPitch + grp * S::NF;
       float a = 0.f;
-#pragma unroll 4
-      for (int j = part; j < n_b; j += P) {
-        const float wj = sh[j];
-        if (wj != 0.f) a += wj * vs[(size_t)j * D];
-      }
-      accbuf[t] = a;
+#pragma unroll
+      for (int e = 0; e < S::NF; ++e) a += st.qf[e] * kr[e];
+      a += __shfl_xor(a, 16, 64);
+      a += __shfl_xor(a, 32, 64);
+      sv[key] = a * kScale2;
+      tmax = fmaxf(tmax, sv[key]);
     }
-  }
-  __syncthreads();
-  if constexpr (CORR) {
-    if (c2 > -INFINITY && t < D) {
-      float s = 0.f;
+    const float mnew = fmaxf(st.mrow, tmax);
+    const float alpha = exp2f(st.mrow - mnew);
+    float psum = 0.f;
 #pragma unroll
-      for (int part = 0; part < 256 / D; ++part) s += accbuf[part * D + t];
-      qbar[t] = s;   // q_bar is no longer needed: it now holds A_i
+    for (int e = 0; e < S::NF; ++e) st.of[e] *= alpha;
+#pragma unroll
+    for (int key = 0; key < 64; ++key) {
+      const float pvv = exp2f(sv[key] - mnew);
+      psum += pvv;
+      const float* vr = stV + key * Gm::kVPitch + grp * S::NF;
+#pragma unroll
+      for (int e = 0; e < S::NF; ++e) st.of[e] += pvv * vr[e];
     }
+    st.lrow = st.lrow * alpha + psum;
+    st.mrow = mnew;
   }
+}
 
-  // ---- 5. inner loop: exact attention on the kept blocks -------------------
-  float mrow = -INFINITY, lrow = 0.f;
-  constexpr int NACC = std::is_same<T, __bf16>::value ? D / 16 : 1;
-  f32x4 oacc[NACC];
-  float of[std::is_same<T, float>::value ? D / 4 : 1];
-#pragma unroll
-  for (int i = 0; i < NACC; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(of) / sizeof(float)); ++i) of[i] = 0.f;
-
-  for (int g = 0; g < p.n_words; ++g) {
-    uint64_t word = masks[g];
-    while (word) {
-      const int j = g * 64 + (int)__builtin_ctzll(word);
-      word &= word - 1;
-      const T* Kj = Kg + (size_t)j * kBlock * D;
-      const T* Vj = Vg + (size_t)j * kBlock * D;
-      __syncthreads();   // previous tile fully consumed
-      if constexpr (std::is_same<T, __bf16>::value) {
-        // K_j natural [key][d]
-        constexpr int CH = D / 8;
-#pragma unroll
-        for (int c = t; c < 64 * CH; c += 256) {
-          const int r = c / CH, cc = c % CH;
-          *reinterpret_cast<uint4*>(stK + r * G::kKPitch + cc * 8) =
-              reinterpret_cast<const uint4*>(Kj + (size_t)r * D)[cc];
-        }
-        // V_j transposed [d][key]: lane takes KPT keys x 8 dims
-        constexpr int KPT = D / 32;          // 4 at d = 128, 2 at d = 64
-        const int dc = t % CH, kg = t / CH;  // kg in [0, 64 / KPT)
-        uint4 raw[KPT];
-#pragma unroll
-        for (int r = 0; r < KPT; ++r)
-          raw[r] = reinterpret_cast<const uint4*>(Vj + (size_t)(kg * KPT + r) * D)[dc];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          unsigned short h[KPT];
-#pragma unroll
-          for (int r = 0; r < KPT; ++r) {
-            const uint32_t word32 = (&raw[r].x)[e >> 1];
-            h[r] = (unsigned short)((e & 1) ? (word32 >> 16) : (word32 & 0xffffu));
-          }
-          T* dst = stV + (dc * 8 + e) * G::kVPitch + kg * KPT;
-          if constexpr (KPT == 4) {
-            *reinterpret_cast<uint2*>(dst) =
-                make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-          } else {
-            *reinterpret_cast<uint32_t*>(dst) = h[0] | ((uint32_t)h[1] << 16);
-          }
-        }
-      } else {
-        constexpr int CH = D / 4;
-        for (int c = t; c < 64 * CH; c += 256) {
-          const int r = c / CH, cc = c % CH;
-          *reinterpret_cast<float4*>(stK + r * G::kKPitch + cc * 4) =
-              reinterpret_cast<const float4*>(Kj + (size_t)r * D)[cc];
-          *reinterpret_cast<float4*>(stV + r * G::kVPitch + cc * 4) =
-              reinterpret_cast<const float4*>(Vj + (size_t)r * D)[cc];
-        }
-      }
-      __syncthreads();
-
-      if constexpr (std::is_same<T, __bf16>::value) {
-        // S^T (64 keys x 16 queries of this wave): 4 key tiles of 16
-        f32x4 s[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                stK + (kt * 16 + (lane & 15)) * G::kKPitch + ks * 32 + grp * 8);
-            s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], s[kt], 0, 0, 0);
-          }
-        }
-        // online softmax (base 2): lane holds keys kt*16 + grp*4 + i of query `row`
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[kt][i]);
-        tmax *= kScale2;
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mnew = fmaxf(mrow, tmax);
-        const float alpha = exp2f(mrow - mnew);
-        float psum = 0.f;
-        bf16x8 pop[2];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pv = exp2f(s[kt][i] * kScale2 - mnew);
-            psum += pv;
-            pop[kt >> 1][(kt & 1) * 4 + i] = to_bf16(pv);
-          }
-        lrow = lrow * alpha + psum;
-        mrow = mnew;
-#pragma unroll
-        for (int dt = 0; dt < NACC; ++dt) oacc[dt] *= alpha;
-        // O^T (d x 16 queries) += V^T (d x 64 keys) P^T: two k-steps of 32 keys
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-          for (int dt = 0; dt < NACC; ++dt) {
-            const T* src = stV + (dt * 16 + (lane & 15)) * G::kVPitch + ks * 32 + grp * 4;
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 16);
-            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[ks], oacc[dt], 0, 0, 0);
-          }
-        }
-      } else {
-        // fp32: 4 lanes per query row, each a quarter of the head dims
-        float sv[64];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int key = 0; key < 64; ++key) {
-          const float* kr = stK + key * G::kKPitch + grp * (D / 4);
-          float a = 0.f;
-#pragma unroll
-          for (int e = 0; e < D / 4; ++e) a += qf[e] * kr[e];
-          a += __shfl_xor(a, 16, 64);
-          a += __shfl_xor(a, 32, 64);
-          sv[key] = a * kScale2;
-          tmax = fmaxf(tmax, sv[key]);
-        }
-        const float mnew = fmaxf(mrow, tmax);
-        const float alpha = exp2f(mrow - mnew);
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < D / 4; ++e) of[e] *= alpha;
-#pragma unroll
-        for (int key = 0; key < 64; ++key) {
-          const float pv = exp2f(sv[key] - mnew);
-          psum += pv;
-          const float* vr = stV + key * G::kVPitch + grp * (D / 4);
-#pragma unroll
-          for (int e = 0; e < D / 4; ++e) of[e] += pv * vr[e];
-        }
-        lrow = lrow * alpha + psum;
-        mrow = mnew;
-      }
-    }
+// out = (O 2^(m-M) + A 2^(c-M)) / (l 2^(m-M) + L 2^(c-M)) for query block qb
+template <typename T, int D>
+__device__ __forceinline__ void epilogue(ExactState<T, D>& st, const FusedParams& p, long long bh, int qb,
+                                         int g, int row, int lane, const float* qa, const float* misc) {
+  using S = ExactState<T, D>;
+  const int grp = lane >> 4;
+  float l = st.lrow;
+  if constexpr (S::kBF) {
+    l += __shfl_xor(l, 16, 64);   // lanes of one row held partial key sums
+    l += __shfl_xor(l, 32, 64);
   }
-
-  // ---- 6. epilogue: merge exact and virtual terms, normalise ---------------
-  if constexpr (std::is_same<T, __bf16>::value) {
-    lrow += __shfl_xor(lrow, 16, 64);   // lanes of one row held partial key sums
-    lrow += __shfl_xor(lrow, 32, 64);
-  }
-  __syncthreads();   // A_i in qbar[] is visible
-  const float M = fmaxf(mrow, c2);
-  const float fo = (mrow == -INFINITY) ? 0.f : exp2f(mrow - M);
+  const float c2 = misc[kC2 + g], Lg = misc[kL + g];
+  const float M = fmaxf(st.mrow, c2);
+  const float fo = (st.mrow == -INFINITY) ? 0.f : exp2f(st.mrow - M);
   const float fc = (c2 == -INFINITY) ? 0.f : exp2f(c2 - M);
-  const float den = lrow * fo + Lsum * fc;
+  const float den = l * fo + Lg * fc;
   const float inv = den > 0.f ? 1.0f / den : 0.f;
-  T* orow = static_cast<T*>(p.out) + ((size_t)bh * p.N + (size_t)qi * kBlock + row) * D;
-  if constexpr (std::is_same<T, __bf16>::value) {
+  T* orow = static_cast<T*>(p.out) + ((size_t)bh * p.N + (size_t)qb * kBlock + row) * D;
+  if constexpr (S::kBF) {
 #pragma unroll
-    for (int dt = 0; dt < NACC; ++dt) {
+    for (int dt = 0; dt < S::NACC; ++dt) {
       const int d0 = dt * 16 + grp * 4;
       float o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float a = (c2 > -INFINITY) ? qbar[d0 + i] * fc : 0.f;
-        o[i] = (oacc[dt][i] * fo + a) * inv;
+        const float a = (c2 > -INFINITY) ? qa[(d0 + i) * kGMax + g] * fc : 0.f;
+        o[i] = (st.oacc[dt][i] * fo + a) * inv;
       }
       bf16x4 ob = {to_bf16(o[0]), to_bf16(o[1]), to_bf16(o[2]), to_bf16(o[3])};
       *reinterpret_cast<bf16x4*>(orow + d0) = ob;
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < D / 4; e += 4) {
-      const int d0 = grp * (D / 4) + e;
+    for (int e = 0; e < S::NF; e += 4) {
+      const int d0 = grp * S::NF + e;
       float4 o;
       float* op = &o.x;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float a = (c2 > -INFINITY) ? qbar[d0 + i] * fc : 0.f;
-        op[i] = (of[e + i] * fo + a) * inv;
+        const float a = (c2 > -INFINITY) ? qa[(d0 + i) * kGMax + g] * fc : 0.f;
+        op[i] = (st.of[e + i] * fo + a) * inv;
       }
       *reinterpret_cast<float4*>(orow + d0) = o;
     }
   }
 }
 
+template <typename T, int D, bool CORR>
+__global__ __launch_bounds__(256) void fused_kernel(FusedParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  using Gm = Geom<T, D>;
+  using L = Lds<T, D>;
+  constexpr float kInvSqrtD = inv_sqrt(D);
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int n_b = p.n_b, nbp = p.n_b_pad, n_words = p.n_words;
+
+  // XCD-aware mapping: hardware deals workgroups round-robin over the 8 XCDs;
+  // give XCD x the contiguous run of work items [x*per_xcd, (x+1)*per_xcd).
+  const long long wgid = blockIdx.x;
+  const long long item = (wgid & 7) * p.per_xcd + (wgid >> 3);
+  if (item >= p.items) return;   // uniform over the workgroup
+  const long long bh = item / p.n_groups;
+  const int qi0 = (int)(item - bh * p.n_groups) * p.G;
+  const int nG = min(p.G, n_b - qi0);
+
+  constexpr bool kBF = std::is_same<T, __bf16>::value;
+  __shared__ __attribute__((aligned(16))) unsigned char sbufA[Gm::kBufBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sbufB[Gm::kBuffers == 2 ? Gm::kBufBytes : 16];
+  uint64_t* masks = reinterpret_cast<uint64_t*>(lds + L::masks());          // [G][n_words]
+  float* qa = reinterpret_cast<float*>(lds + L::qa(p.G, n_words));          // [D][kGMax]
+  float* acc = reinterpret_cast<float*>(lds + L::acc(p.G, n_words));        // [4][kGMax][D]
+  float* misc = reinterpret_cast<float*>(lds + L::misc(p.G, n_words));
+  // proxy rows of the routing phase, overlaid on the tile buffers
+  float* shr[kGMax];
+  {
+    const int rpb = L::rows_per_buf(nbp);
+#pragma unroll
+    for (int g = 0; g < kGMax; ++g)
+      shr[g] = g < rpb ? reinterpret_cast<float*>(sbufA) + g * nbp
+                       : reinterpret_cast<float*>(sbufB) + (g - rpb) * nbp;
+  }
+
+  const T* Qh = static_cast<const T*>(p.q) + (size_t)bh * p.N * D;
+  const T* Kh = static_cast<const T*>(p.k) + (size_t)bh * p.N * D;
+  const T* Vh = static_cast<const T*>(p.v) + (size_t)bh * p.N * D;
+
+  // ---- 1. q_bar of the G query blocks ---------------------------------------
+  {
+    using V16 = Vec16<T>;
+    constexpr int E = V16::kN, CH = D / E, RPT = 64 * CH / 256, RSTEP = 256 / CH;
+    const int cc = t % CH, r0 = t / CH;
+    for (int g = 0; g < nG; ++g) {
+      const T* Qb = Qh + (size_t)(qi0 + g) * kBlock * D;
+      float s[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        float f[E];
+        V16::to_float(reinterpret_cast<const typename V16::raw*>(Qb + (size_t)(r0 + RSTEP * i) * D)[cc], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[e] += f[e];
+      }
+#pragma unroll
+      for (int o = CH; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[e] += __shfl_xor(s[e], o, 64);
+      if (lane < CH)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[(w * kGMax + g) * D + cc * E + e] = s[e];
+    }
+  }
+  __syncthreads();
+  if (t < D) {
+#pragma unroll
+    for (int g = 0; g < kGMax; ++g) {
+      float s = 0.f;
+      if (g < nG)
+        s = ((acc[(0 * kGMax + g) * D + t] + acc[(1 * kGMax + g) * D + t]) +
+             (acc[(2 * kGMax + g) * D + t] + acc[(3 * kGMax + g) * D + t])) * (1.0f / kBlock);
+      qa[t * kGMax + g] = s;   // zero for g >= nG: those proxy rows are never used
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. tau = mu + beta sigma for each block (closed form) ----------------
+  {
+    const float* C = p.kcov + (size_t)bh * D * D;
+    const float* m = p.kmean + (size_t)bh * D;
+    constexpr int P = 256 / D;
+    const int r = t % D, part = t / D;
+    float y[kGMax] = {0.f, 0.f, 0.f, 0.f};
+    for (int c = part; c < D; c += P) {
+      const float cv = C[(size_t)c * D + r];
+      const float4 qv = *reinterpret_cast<const float4*>(qa + c * kGMax);
+      y[0] += cv * qv.x; y[1] += cv * qv.y; y[2] += cv * qv.z; y[3] += cv * qv.w;
+    }
+    const float4 qr = *reinterpret_cast<const float4*>(qa + r * kGMax);
+    const float mr = part == 0 ? m[r] : 0.f;
+    float v8[8] = {qr.x * y[0], qr.y * y[1], qr.z * y[2], qr.w * y[3],
+                   qr.x * mr, qr.y * mr, qr.z * mr, qr.w * mr};
+    block_sum_n<8>(v8, misc);
+    if (t < nG) {
+      const float qcq = misc[kTot + t], qm = misc[kTot + 4 + t];
+      const float mu = qm * kInvSqrtD;
+      const float sigma = sqrtf(fmaxf(qcq, 0.f) * (1.0f / D));
+      float tau;
+      if (p.beta_mode == kBetaMinusInf) tau = -INFINITY;
+      else if (p.beta_mode == kBetaPlusInf) tau = INFINITY;
+      else tau = mu + p.beta * sigma;
+      misc[kTau + t] = tau;
+    }
+  }
+
+  // ---- 3a. outer loop: proxy scores of every key block for the G blocks ------
+  {
+    const float* kt = p.kbar_t + (size_t)bh * D * nbp;
+    for (int j4 = 4 * t; j4 < n_b; j4 += 1024) {
+      float a[kGMax][4];
+#pragma unroll
+      for (int g = 0; g < kGMax; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[g][e] = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < D; ++c) {
+        const float4 kv = *reinterpret_cast<const float4*>(kt + (size_t)c * nbp + j4);
+        const float4 qv = *reinterpret_cast<const float4*>(qa + c * kGMax);
+        const float qg[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+        for (int g = 0; g < kGMax; ++g) {
+          a[g][0] += qg[g] * kv.x; a[g][1] += qg[g] * kv.y;
+          a[g][2] += qg[g] * kv.z; a[g][3] += qg[g] * kv.w;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < kGMax; ++g) {
+        if (g < nG) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j4 + e < n_b) shr[g][j4 + e] = a[g][e] * kInvSqrtD;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 3b. strict test against tau -> one 64-bit word per 64 key blocks ------
+  {
+    float cmax[kGMax] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float kept[kGMax] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < kGMax; ++g) {
+      if (g < nG) {
+        const float tau = misc[kTau + g];
+        for (int wi = w; wi < n_words; wi += 4) {
+          const int j = wi * 64 + lane;
+          const bool valid = j < n_b;
+          const float s = valid ? shr[g][j] : 0.f;
+          const bool keep = valid && (s > tau);
+          const uint64_t word = __ballot(keep);
+          if (valid && !keep) cmax[g] = fmaxf(cmax[g], s);
+          if (lane == 0) masks[g * n_words + wi] = word;
+          kept[g] += (lane == 0) ? (float)__popcll(word) : 0.f;
+        }
+      }
+    }
+    block_max_n<kGMax>(cmax, misc);
+    if (t < kGMax) {
+      misc[kC2 + t] = (CORR && misc[kTot + t] > -INFINITY) ? misc[kTot + t] * kLog2e : -INFINITY;
+      misc[kL + t] = 0.f;
+    }
+    block_sum_n<kGMax>(kept, misc);
+    for (int g = 0; g < nG; ++g) {
+      const long long qrow = bh * n_b + qi0 + g;
+      if (t == 0) {
+        if (p.kept_per_row) p.kept_per_row[qrow] = (int)misc[kTot + g];
+        if (p.tau_out) p.tau_out[qrow] = misc[kTau + g];
+      }
+      if (p.mask_bits)
+        for (int wi = t; wi < n_words; wi += 256) p.mask_bits[qrow * n_words + wi] = masks[g * n_words + wi];
+    }
+  }
+
+  // ---- 4. correction: unselected blocks as 64 virtual tokens ----------------
+  if constexpr (CORR) {
+    float c2[kGMax];
+#pragma unroll
+    for (int g = 0; g < kGMax; ++g) c2[g] = misc[kC2 + g];
+    float lp[kGMax] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = t; j < n_b; j += 256) {
+#pragma unroll
+      for (int g = 0; g < kGMax; ++g) {
+        if (g < nG) {
+          const bool keep = (masks[g * n_words + (j >> 6)] >> (j & 63)) & 1ull;
+          const float wj = (keep || c2[g] == -INFINITY) ? 0.f : exp2f(shr[g][j] * kLog2e - c2[g]);
+          shr[g][j] = wj;
+          lp[g] += wj;
+        }
+      }
+    }
+    block_sum_n<kGMax>(lp, misc);   // barrier: the weights are complete
+    if (t < kGMax) misc[kL + t] = misc[kTot + t] * (float)kBlock;
+    constexpr int P = 256 / D;
+    const int col = t % D, part = t / D;
+    const float* vs = p.vsum + (size_t)bh * n_b * D + col;
+    float a[kGMax] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = part; j < n_b; j += P) {
+      float wj[kGMax];
+      bool any = false;
+#pragma unroll
+      for (int g = 0; g < kGMax; ++g) {
+        wj[g] = g < nG ? shr[g][j] : 0.f;
+        any |= wj[g] != 0.f;
+      }
+      if (any) {
+        const float x = vs[(size_t)j * D];
+#pragma unroll
+        for (int g = 0; g < kGMax; ++g) a[g] += wj[g] * x;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kGMax; ++g) acc[(part * kGMax + g) * D + col] = a[g];
+    __syncthreads();
+    if (t < D) {
+#pragma unroll
+      for (int g = 0; g < kGMax; ++g) {
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < P; ++q) s += acc[(q * kGMax + g) * D + t];
+        qa[t * kGMax + g] = s;   // q_bar is no longer needed: qa now holds A
+      }
+    }
+  }
+  __syncthreads();   // masks, A, L, c2 visible; the proxy rows are dead
+
+  // ---- 5. inner loop: exact attention on the kept tiles ---------------------
+  ExactState<T, D> st;
+  const int row = 16 * w + (lane & 15);   // this lane's query row within a block
+  int cg = 0;
+  reset_block<T, D>(st, Qh + ((size_t)qi0 * kBlock + row) * D, lane);
+  Tile cur = next_tile(Tile{0, -1}, masks, nG, n_words);
+  // finish every query block before block `upto` (no kept tiles left for them)
+#define SOL_FINISH_BEFORE(upto)                                                   \
+  while (cg < (upto)) {                                                           \
+    epilogue<T, D>(st, p, bh, qi0 + cg, cg, row, lane, qa, misc);                 \
+    ++cg;                                                                         \
+    reset_block<T, D>(st, Qh + ((size_t)(qi0 + cg) * kBlock + row) * D, lane);    \
+  }
+  if constexpr (kBF) {
+    // one barrier per tile: wait for this lane's loads of `cur`, barrier (all
+    // lanes' loads landed; every wave finished the previous tile, so the other
+    // buffer is free), start loading `nxt` into it, compute `cur`
+#define SOL_STEP(CURB, NEXTB)                                                     \
+    {                                                                             \
+      SOL_FINISH_BEFORE(cur.g)                                                    \
+      const Tile nxt = next_tile(cur, masks, nG, n_words);                        \
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                           \
+      __syncthreads();                                                            \
+      if (nxt.g >= 0) issue_tile<D>(NEXTB, Kh, p.vt, bh, n_b, nxt.j, t);          \
+      compute_tile<T, D>(st, CURB, lane);                                         \
+      cur = nxt;                                                                  \
+    }
+    if (cur.g >= 0) issue_tile<D>(sbufA, Kh, p.vt, bh, n_b, cur.j, t);
+    while (cur.g >= 0) {
+      SOL_STEP(sbufA, sbufB)
+      if (cur.g < 0) break;
+      SOL_STEP(sbufB, sbufA)
+    }
+#undef SOL_STEP
+  } else {
+    while (cur.g >= 0) {
+      SOL_FINISH_BEFORE(cur.g)
+      const Tile nxt = next_tile(cur, masks, nG, n_words);
+      __syncthreads();
+      commit_f32<D>(reinterpret_cast<float*>(sbufA), reinterpret_cast<float*>(sbufA + Gm::kKBytes),
+                    reinterpret_cast<const float*>(Kh), reinterpret_cast<const float*>(Vh), cur.j, t);
+      __syncthreads();
+      compute_tile<T, D>(st, sbufA, lane);
+      cur = nxt;
+    }
+  }
+#undef SOL_FINISH_BEFORE
+  while (cg < nG) {
+    epilogue<T, D>(st, p, bh, qi0 + cg, cg, row, lane, qa, misc);
+    ++cg;
+    if (cg < nG) reset_block<T, D>(st, Qh + ((size_t)(qi0 + cg) * kBlock + row) * D, lane);
+  }
+}
+
 template <typename T, int D>
 hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
+  const FusedGeom g = fused_geom(s, std::is_same<T, __bf16>::value ? Dtype::BF16 : Dtype::F32);
+  if (g.G < 1) return hipErrorInvalidValue;   // n_b too large for the LDS proxy rows
   FusedParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.out = a.out;
+  p.vt = a.ws.vt;
   p.kbar_t = a.ws.kbar_t; p.vsum = a.ws.vsum; p.kmean = a.ws.kmean; p.kcov = a.ws.kcov;
-  p.n_b = s.n_b; p.n_b_pad = s.n_b_pad; p.n_words = s.n_words; p.N = s.N;
+  p.n_b = s.n_b; p.n_b_pad = s.n_b_pad; p.n_words = s.n_words;
+  p.G = g.G; p.n_groups = g.n_groups; p.items = g.items; p.per_xcd = g.per_xcd;
+  p.N = s.N;
   p.beta = a.beta; p.beta_mode = a.beta_mode;
   p.kept_per_row = a.kept_per_row; p.mask_bits = a.mask_bits; p.tau_out = a.tau;
-  const int lds = Lds<T, D>::bytes(s.n_b);
-  const dim3 grid((unsigned)(s.BH() * s.n_b));
+  const dim3 grid((unsigned)(8 * g.per_xcd));
   if (a.correction) {
     auto k = fused_kernel<T, D, true>;
-    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, dim3(256), lds, st, p);
+    hipLaunchKernelGGL(k, grid, dim3(256), g.lds_bytes, st, p);
   } else {
     auto k = fused_kernel<T, D, false>;
-    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, dim3(256), lds, st, p);
+    hipLaunchKernelGGL(k, grid, dim3(256), g.lds_bytes, st, p);
   }
   return hipGetLastError();
 }
 
+template <typename T, int D>
+FusedGeom geom_impl(const Shape& s) {
+  using L = Lds<T, D>;
+  FusedGeom g;
+  const int cap = L::rows_per_buf(s.n_b_pad) * Geom<T, D>::kBuffers;   // proxy rows that fit
+  g.G = cap < 1 ? 0 : (cap < kGMax ? cap : kGMax);
+  g.n_groups = g.G ? (s.n_b + g.G - 1) / g.G : 0;
+  g.items = s.BH() * g.n_groups;
+  g.per_xcd = (g.items + 7) / 8;
+  g.lds_bytes = L::bytes(g.G, s.n_words);
+  return g;
+}
+
 }  // namespace
 
-int fused_lds_bytes(Dtype dt, int d, int n_b) {
-  if (dt == Dtype::BF16) return d == 64 ? Lds<__bf16, 64>::bytes(n_b) : Lds<__bf16, 128>::bytes(n_b);
-  return d == 64 ? Lds<float, 64>::bytes(n_b) : Lds<float, 128>::bytes(n_b);
+FusedGeom fused_geom(const Shape& s, Dtype dt) {
+  if (dt == Dtype::BF16) return s.d == 64 ? geom_impl<__bf16, 64>(s) : geom_impl<__bf16, 128>(s);
+  return s.d == 64 ? geom_impl<float, 64>(s) : geom_impl<float, 128>(s);
 }
 
 hipError_t launch_fused(const Shape& s, Dtype dt, const FusedArgs& a, hipStream_t stream) {

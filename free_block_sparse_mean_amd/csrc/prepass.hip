@@ -5,18 +5,23 @@
 //   k_bar_j = mean of the 64 keys of block j         (row-major and transposed)
 //   vsum_j  = sum of the 64 values of block j        (= 64 * v_bar_j)
 //   m       = mean over j of k_bar_j
-//   C       = (1/n_b) sum_j (k_bar_j - m)(k_bar_j - m)^T   (centred, population)
+//   C       = (1/n_b) sum_j k_bar_j k_bar_j^T - m m^T   (population covariance)
+// and, for bf16 inputs, a copy of V with every 64 x d block transposed to
+// d x 64 (the layout the fused pass stages for its P.V products).
 // Sources: page "Sol-Attn: l'attenzione sparsa che sceglie al volo"
 // (paithon.it), section "Perche l'attenzione pesa tanto nei video" for the
 // 64-token block means, section "Una soglia per ogni riga" (last paragraph)
-// for mu_i/sigma_i from the key-summary mean and d x d second moments, and
-// section "Scegliere mentre si calcola" for the block-mean values the
-// correction reuses.
+// for mu_i/sigma_i from the mean of the compressed keys and their d x d
+// second-moment matrix, and section "Scegliere mentre si calcola" for the
+// block-mean values the correction reuses.
 //
-// Bound: HBM bandwidth. block_sums streams 2*N*d input elements per head with
-// 16-byte loads, one wave per block; the mean/covariance kernels touch only
-// the n_b x d summaries (L2-resident) and accumulate in double so that the
-// closed-form threshold carries no cancellation from the key mean.
+// Bound: HBM bandwidth. block_sums streams 2*N*d input elements per head
+// with 16-byte loads, one wave per block (and writes N*d transposed values
+// for bf16). The moment kernels touch only the n_b x d summaries
+// (L2-resident) and accumulate in double, so forming C from second moments
+// loses nothing to cancellation at fp32 resolution.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "sol_internal.hpp"
 
@@ -25,21 +30,26 @@ namespace {
 
 // One wave per key block: lane (rg, cc) sums rows rg, rg+RG, ... of 16-byte
 // column chunk cc for K and V, then the row groups are folded by xor-shuffles.
-template <typename T, int D>
+// With WRITE_VT the wave also stages its V block in LDS and writes it back
+// transposed ([d][64] per block).
+template <typename T, int D, bool WRITE_VT>
 __global__ __launch_bounds__(256) void block_sums_kernel(const T* __restrict__ k,
                                                          const T* __restrict__ v,
                                                          float* __restrict__ kbar,
                                                          float* __restrict__ vsum,
+                                                         __bf16* __restrict__ vt,
                                                          int n_b, long long N) {
   using V = Vec16<T>;
   constexpr int E = V::kN;     // elements per 16-byte chunk
   constexpr int CH = D / E;    // chunks per row
   constexpr int RG = 64 / CH;  // row groups
   constexpr int RPL = 64 / RG; // rows per lane
-  const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int kPitch = D;    // unpadded: row writes are whole 16-byte chunks
+  __shared__ __attribute__((aligned(16))) __bf16 stage[WRITE_VT ? 4 : 1][WRITE_VT ? 64 * kPitch : 8];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int j = blockIdx.x * 4 + wv;
   const long long bh = blockIdx.y;
-  if (j >= n_b) return;
+  if (j >= n_b) return;   // whole wave leaves; no workgroup barrier below
   const int cc = lane % CH, rg = lane / CH;
   const size_t base = ((size_t)bh * N + (size_t)j * kBlock) * D;
   const typename V::raw* pk = reinterpret_cast<const typename V::raw*>(k + base) + cc;
@@ -50,11 +60,14 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const T* __restrict__ k
 #pragma unroll 8
   for (int i = 0; i < RPL; ++i) {
     const int r = rg + RG * i;
+    const typename V::raw rv = pv[(size_t)r * CH];
     float fk[E], fv[E];
     V::to_float(pk[(size_t)r * CH], fk);
-    V::to_float(pv[(size_t)r * CH], fv);
+    V::to_float(rv, fv);
 #pragma unroll
     for (int e = 0; e < E; ++e) { ak[e] += fk[e]; av[e] += fv[e]; }
+    if constexpr (WRITE_VT)
+      *reinterpret_cast<typename V::raw*>(&stage[wv][r * kPitch + cc * E]) = rv;
   }
 #pragma unroll
   for (int o = CH; o < 64; o <<= 1) {
@@ -73,51 +86,48 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const T* __restrict__ k
       vs[e] = av[e];
     }
   }
-}
-
-// m = mean_j k_bar_j per head, accumulated in double.
-template <int D>
-__global__ __launch_bounds__(256) void key_mean_kernel(const float* __restrict__ kbar,
-                                                       float* __restrict__ kmean,
-                                                       double* __restrict__ kmean64, int n_b) {
-  constexpr int P = 256 / D;
-  __shared__ double red[256];
-  const int t = threadIdx.x, c = t % D, p = t / D;
-  const long long bh = blockIdx.x;
-  const float* kb = kbar + (size_t)bh * n_b * D;
-  double acc = 0.0;
-  for (int j = p; j < n_b; j += P) acc += (double)kb[(size_t)j * D + c];
-  red[t] = acc;
-  __syncthreads();
-  if (t < D) {
-    double s = 0.0;
+  if constexpr (WRITE_VT) {
+    // The wave wrote the whole 64 x D block; LDS accesses of one wave are
+    // performed in order, so a wave-level fence suffices before reading.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // output chunk (d, kc): keys kc*8 .. kc*8+7 of head dim d, 16 bytes;
+    // consecutive lanes take consecutive d so the LDS column reads do not
+    // collide in banks
+    __bf16* dst = vt + ((size_t)bh * n_b + j) * D * 64;
+    for (int c = lane; c < D * 8; c += 64) {
+      const int d = c % D, kc = c / D;
+      uint32_t w[4];
 #pragma unroll
-    for (int q = 0; q < P; ++q) s += red[q * D + t];
-    const double m = s / (double)n_b;
-    kmean64[(size_t)bh * D + t] = m;
-    kmean[(size_t)bh * D + t] = (float)m;
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t lo = __builtin_bit_cast(unsigned short, stage[wv][(kc * 8 + 2 * h) * kPitch + d]);
+        const uint32_t hi = __builtin_bit_cast(unsigned short, stage[wv][(kc * 8 + 2 * h + 1) * kPitch + d]);
+        w[h] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(dst + (size_t)d * 64 + kc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
 }
 
-// Partial centred second moments over one chunk of kCovChunk key blocks, in
-// double; also writes the transposed summaries kbar_t for the chunk.
+// Partial first and second moments of the key summaries over one chunk of
+// kCovChunk blocks, in double; also writes the transposed summaries kbar_t.
 template <int D>
-__global__ __launch_bounds__(256) void cov_partial_kernel(const float* __restrict__ kbar,
-                                                          const double* __restrict__ kmean64,
-                                                          float* __restrict__ kbar_t,
-                                                          double* __restrict__ cov_part,
-                                                          int n_b, int n_b_pad, int parts) {
+__global__ __launch_bounds__(256) void moments_partial_kernel(const float* __restrict__ kbar,
+                                                              float* __restrict__ kbar_t,
+                                                              double* __restrict__ s1_part,
+                                                              double* __restrict__ s2_part,
+                                                              int n_b, int n_b_pad, int parts) {
   constexpr int TJ = 32;       // key blocks staged per step
   constexpr int R = D / 16;    // outputs per thread along each dimension
   __shared__ float tile[TJ][D + 1];
-  __shared__ double mloc[D];
   const int t = threadIdx.x, ty = t / 16, tx = t % 16;
   const long long bh = blockIdx.y;
   const int part = blockIdx.x;
   const int j0 = part * kCovChunk;
   const int j1 = min(n_b, j0 + kCovChunk);
-  if (t < D) mloc[t] = kmean64[(size_t)bh * D + t];
   double acc[R][R];
+  double s1 = 0.0;
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -139,13 +149,14 @@ __global__ __launch_bounds__(256) void cov_partial_kernel(const float* __restric
       double a[R], b[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        a[r] = (double)tile[jj][ty * R + r] - mloc[ty * R + r];
-        b[r] = (double)tile[jj][tx * R + r] - mloc[tx * R + r];
+        a[r] = (double)tile[jj][ty * R + r];
+        b[r] = (double)tile[jj][tx * R + r];
       }
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int s = 0; s < R; ++s) acc[r][s] += a[r] * b[s];
+      if (t < D) s1 += (double)tile[jj][t];
     }
   }
   // zero the row padding of kbar_t once per head
@@ -155,43 +166,54 @@ __global__ __launch_bounds__(256) void cov_partial_kernel(const float* __restric
       kbar_t[((size_t)bh * D + c) * n_b_pad + j] = 0.f;
     }
   }
-  double* outp = cov_part + ((size_t)bh * parts + part) * D * D;
+  double* outp = s2_part + ((size_t)bh * parts + part) * D * D;
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int s = 0; s < R; ++s) outp[(size_t)(ty * R + r) * D + tx * R + s] = acc[r][s];
+  if (t < D) s1_part[((size_t)bh * parts + part) * D + t] = s1;
 }
 
-// C = (sum of the partials in chunk order) / n_b, stored as float.
+// m = (sum of the S1 partials) / n_b and C = (sum of the S2 partials) / n_b - m m^T,
+// partials summed in chunk order (deterministic), stored as float.
 template <int D>
-__global__ __launch_bounds__(256) void cov_reduce_kernel(const double* __restrict__ cov_part,
-                                                         float* __restrict__ kcov, int n_b,
-                                                         int parts) {
+__global__ __launch_bounds__(256) void moments_reduce_kernel(const double* __restrict__ s1_part,
+                                                             const double* __restrict__ s2_part,
+                                                             float* __restrict__ kmean,
+                                                             float* __restrict__ kcov, int n_b,
+                                                             int parts) {
+  __shared__ double m[D];
   const long long bh = blockIdx.y;
-  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int t = threadIdx.x;
+  if (t < D) {
+    double s = 0.0;
+    for (int p = 0; p < parts; ++p) s += s1_part[((size_t)bh * parts + p) * D + t];
+    m[t] = s / (double)n_b;
+    if (blockIdx.x == 0) kmean[(size_t)bh * D + t] = (float)m[t];
+  }
+  __syncthreads();
+  const int e = blockIdx.x * 256 + t;
   if (e >= D * D) return;
   double s = 0.0;
-  for (int p = 0; p < parts; ++p) s += cov_part[((size_t)bh * parts + p) * D * D + e];
-  kcov[(size_t)bh * D * D + e] = (float)(s / (double)n_b);
+  for (int p = 0; p < parts; ++p) s += s2_part[((size_t)bh * parts + p) * D * D + e];
+  kcov[(size_t)bh * D * D + e] = (float)(s / (double)n_b - m[e / D] * m[e % D]);
 }
 
 template <typename T, int D>
 hipError_t prepass_impl(const Shape& s, const void* k, const void* v, const Workspace& ws,
                         hipStream_t st) {
   const unsigned bh = (unsigned)s.BH();
-  hipLaunchKernelGGL((block_sums_kernel<T, D>), dim3((s.n_b + 3) / 4, bh), dim3(256), 0, st,
-                     static_cast<const T*>(k), static_cast<const T*>(v), ws.kbar, ws.vsum, s.n_b,
-                     (long long)s.N);
+  constexpr bool kVT = std::is_same<T, __bf16>::value;
+  hipLaunchKernelGGL((block_sums_kernel<T, D, kVT>), dim3((s.n_b + 3) / 4, bh), dim3(256), 0, st,
+                     static_cast<const T*>(k), static_cast<const T*>(v), ws.kbar, ws.vsum, ws.vt,
+                     s.n_b, (long long)s.N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((key_mean_kernel<D>), dim3(bh), dim3(256), 0, st, ws.kbar, ws.kmean,
-                     ws.kmean64, s.n_b);
+  hipLaunchKernelGGL((moments_partial_kernel<D>), dim3(s.cov_parts, bh), dim3(256), 0, st, ws.kbar,
+                     ws.kbar_t, ws.s1_part, ws.s2_part, s.n_b, s.n_b_pad, s.cov_parts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((cov_partial_kernel<D>), dim3(s.cov_parts, bh), dim3(256), 0, st, ws.kbar,
-                     ws.kmean64, ws.kbar_t, ws.cov_part, s.n_b, s.n_b_pad, s.cov_parts);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((cov_reduce_kernel<D>), dim3((D * D + 255) / 256, bh), dim3(256), 0, st,
-                     ws.cov_part, ws.kcov, s.n_b, s.cov_parts);
+  hipLaunchKernelGGL((moments_reduce_kernel<D>), dim3((D * D + 255) / 256, bh), dim3(256), 0, st,
+                     ws.s1_part, ws.s2_part, ws.kmean, ws.kcov, s.n_b, s.cov_parts);
   return hipGetLastError();
 }
 

@@ -32,16 +32,27 @@ struct Workspace {
   float* vsum;      // [BH][n_b][d]
   float* kmean;     // [BH][d]
   float* kcov;      // [BH][d][d]
-  double* kmean64;  // [BH][d]            (pre-pass scratch)
-  double* cov_part; // [BH][cov_parts][d][d] (pre-pass scratch)
+  __bf16* vt;       // [BH][n_b][d][64]  V blocks transposed (bf16 inputs only)
+  double* s1_part;  // [BH][cov_parts][d]     (pre-pass scratch)
+  double* s2_part;  // [BH][cov_parts][d][d]  (pre-pass scratch)
 };
 
 struct Layout {
-  size_t kbar_t, kbar, vsum, kmean, kcov, kmean64, cov_part, total;
+  size_t kbar_t, kbar, vsum, kmean, kcov, vt, s1_part, s2_part, total;
 };
 
 Layout make_layout(const Shape& s);
 Workspace bind_workspace(const Shape& s, void* base);
+
+// Launch geometry of the fused pass (shared by the host runtime and tests).
+struct FusedGeom {
+  int G;            // query blocks per workgroup
+  int n_groups;     // ceil(n_b / G) per head
+  long long items;  // BH * n_groups
+  long long per_xcd;  // ceil(items / 8)
+  int lds_bytes;
+};
+FusedGeom fused_geom(const Shape& s, Dtype dt);
 
 struct FusedArgs {
   const void* q;
@@ -61,6 +72,6 @@ struct FusedArgs {
 hipError_t launch_prepass(const Shape& s, Dtype dt, const void* k, const void* v,
                           const Workspace& ws, hipStream_t stream);
 hipError_t launch_fused(const Shape& s, Dtype dt, const FusedArgs& a, hipStream_t stream);
-int fused_lds_bytes(Dtype dt, int d, int n_b);
+
 
 }  // namespace sol

@@ -148,16 +148,28 @@ def iter_heads(w: Workload) -> Iterator[Tuple[int, int, torch.Tensor, torch.Tens
             yield b, h, _to_torch(q, w.dtype), _to_torch(k, w.dtype), _to_torch(v, w.dtype)
 
 
-def make_qkv(w: Workload) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """All heads as host tensors [B, H, N, d] in the workload dtype."""
+def make_qkv(w: Workload, threads: int = 8) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """All heads as host tensors [B, H, N, d] in the workload dtype.
+
+    Heads are drawn in parallel threads; each head has its own seeded stream,
+    so the result does not depend on the thread count.
+    """
+    from concurrent.futures import ThreadPoolExecutor
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     q = torch.empty((w.B, w.H, w.N, w.d), dtype=tdt)
     k = torch.empty_like(q)
     v = torch.empty_like(q)
-    for b, h, qh, kh, vh in iter_heads(w):
-        q[b, h].copy_(qh)
-        k[b, h].copy_(kh)
-        v[b, h].copy_(vh)
+    field = _field(w.grid, w.d, w.seed) if w.kind == "field" else None
+
+    def one(bh):
+        b, h = divmod(bh, w.H)
+        qh, kh, vh = head_qkv(w, b, h, field)
+        q[b, h].copy_(_to_torch(qh, w.dtype))
+        k[b, h].copy_(_to_torch(kh, w.dtype))
+        v[b, h].copy_(_to_torch(vh, w.dtype))
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(one, range(w.B * w.H)))
     return q, k, v
 
 

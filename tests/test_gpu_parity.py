@@ -141,7 +141,12 @@ def test_prepass_summaries(w, gpu_lib):
     ws = gpu_lib.new_workspace(w.B, w.H, w.N, w.d)
     gpu_lib.sol_block_summaries(kd, vd, ws)
     torch.cuda.synchronize()
-    views = {n: t.cpu().double().numpy() for n, t in gpu_lib.workspace_views(ws, w.B, w.H, w.N, w.d).items()}
+    raw = gpu_lib.workspace_views(ws, w.B, w.H, w.N, w.d)
+    if w.dtype == BF:
+        # each 64 x d block of V transposed, bit for bit
+        vt_ref = v.view(w.B, w.H, w.n_blocks, 64, w.d).transpose(-1, -2)
+        assert torch.equal(raw["vt"].cpu(), vt_ref)
+    views = {n: t.cpu().double().numpy() for n, t in raw.items() if n != "vt"}
     for b in range(w.B):
         for h in range(w.H):
             kbar = orc.block_means(k[b, h].float().numpy())

@@ -20,6 +20,9 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the online-softmax rescale and the epilogue
+    # then touch them without accvgpr moves
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -66,7 +66,7 @@ struct FusedParams {
   const float* kmean;
   const float* kcov;
   int n_b, n_b_pad, n_words, G, n_groups;
-  long long items, per_xcd;
+  long long BH, per_xcd;   // per_xcd: work items of one head given to each XCD
   long long N;
   float beta;
   int beta_mode;
@@ -127,6 +127,14 @@ constexpr int kC2 = 44;          // [kGMax] correction max (base 2), -inf if non
 constexpr int kL = 48;           // [kGMax] correction denominator 64 * sum w
 
 constexpr float inv_sqrt(int d) { return d == 64 ? 0.125f : 0.08838834764831845f; }
+
+// 2^x with the hardware v_exp_f32 (results below 2^-126 flush to 0, which a
+// softmax weight can afford); 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Rows rescale their accumulators only when a new tile maximum exceeds the
+// reference by more than this (base-2 exponent): weights then stay <= 2^8.
+constexpr float kRescaleSlack = 8.0f;
 
 // Sum over the workgroup of NV floats per thread; totals land in misc[kTot + v].
 template <int NV>
@@ -291,32 +299,35 @@ __device__ __forceinline__ void compute_tile(ExactState<T, D>& st, const unsigne
     tmax *= kScale2;
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mnew = fmaxf(st.mrow, tmax);
-    const float alpha = exp2f(st.mrow - mnew);
+    // move the reference only when the tile maximum exceeds it by the slack
+    const bool grow = tmax > st.mrow + kRescaleSlack;
+    if (__ballot(grow)) {
+      const float mnew = grow ? tmax : st.mrow;
+      const float alpha = fast_exp2(st.mrow - mnew);   // 0 on the first tile, 1 if !grow
+      st.lrow *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < S::NACC; ++dt) st.oacc[dt] *= alpha;
+      st.mrow = mnew;
+    }
+    const float mref = st.mrow;
     float psum = 0.f;
     bf16x8 pop[2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pvv = exp2f(s[kt][i] * kScale2 - mnew);
+        const float pvv = fast_exp2(__builtin_fmaf(s[kt][i], kScale2, -mref));
         psum += pvv;
         pop[kt >> 1][(kt & 1) * 4 + i] = to_bf16(pvv);
       }
-    st.lrow = st.lrow * alpha + psum;
-    st.mrow = mnew;
-#pragma unroll
-    for (int dt = 0; dt < S::NACC; ++dt) st.oacc[dt] *= alpha;
+    st.lrow += psum;
     // O^T (d x 16 queries) += V^T (d x 64 keys) P^T: two k-steps of 32 keys
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int dt = 0; dt < S::NACC; ++dt) {
-        const int d = dt * 16 + (lane & 15);
-        const int kc = ks * 4 + (grp >> 1), off = (grp & 1) * 8;
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(bV + 16 * v_pos(d, kc) + off);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(bV + 16 * v_pos(d, kc + 2) + off);
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        // keys of k-step ks for this lane group, stored in operand order
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(bV + 16 * v_pos(dt * 16 + (lane & 15), ks * 4 + grp));
         st.oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[ks], st.oacc[dt], 0, 0, 0);
       }
     }
@@ -338,13 +349,13 @@ __device__ __forceinline__ void compute_tile(ExactState<T, D>& st, const unsigne
       tmax = fmaxf(tmax, sv[key]);
     }
     const float mnew = fmaxf(st.mrow, tmax);
-    const float alpha = exp2f(st.mrow - mnew);
+    const float alpha = fast_exp2(st.mrow - mnew);
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < S::NF; ++e) st.of[e] *= alpha;
 #pragma unroll
     for (int key = 0; key < 64; ++key) {
-      const float pvv = exp2f(sv[key] - mnew);
+      const float pvv = fast_exp2(sv[key] - mnew);
       psum += pvv;
       const float* vr = stV + key * Gm::kVPitch + grp * S::NF;
 #pragma unroll
@@ -368,8 +379,8 @@ __device__ __forceinline__ void epilogue(ExactState<T, D>& st, const FusedParams
   }
   const float c2 = misc[kC2 + g], Lg = misc[kL + g];
   const float M = fmaxf(st.mrow, c2);
-  const float fo = (st.mrow == -INFINITY) ? 0.f : exp2f(st.mrow - M);
-  const float fc = (c2 == -INFINITY) ? 0.f : exp2f(c2 - M);
+  const float fo = (st.mrow == -INFINITY) ? 0.f : fast_exp2(st.mrow - M);
+  const float fc = (c2 == -INFINITY) ? 0.f : fast_exp2(c2 - M);
   const float den = l * fo + Lg * fc;
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   T* orow = static_cast<T*>(p.out) + ((size_t)bh * p.N + (size_t)qb * kBlock + row) * D;
@@ -412,13 +423,17 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedParams p) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int n_b = p.n_b, nbp = p.n_b_pad, n_words = p.n_words;
 
-  // XCD-aware mapping: hardware deals workgroups round-robin over the 8 XCDs;
-  // give XCD x the contiguous run of work items [x*per_xcd, (x+1)*per_xcd).
+  // XCD-aware mapping: the hardware deals workgroups round-robin over the 8
+  // XCDs. Each head's n_groups work items are cut into 8 contiguous runs, run
+  // x going to XCD x, and heads are taken in order: all XCDs work on the same
+  // head at a time (its K and V^T stay in the shared Infinity Cache) and each
+  // XCD's L2 sees neighbouring query blocks, which keep similar key blocks.
   const long long wgid = blockIdx.x;
-  const long long item = (wgid & 7) * p.per_xcd + (wgid >> 3);
-  if (item >= p.items) return;   // uniform over the workgroup
-  const long long bh = item / p.n_groups;
-  const int qi0 = (int)(item - bh * p.n_groups) * p.G;
+  const long long r = wgid >> 3;
+  const long long bh = r / p.per_xcd;
+  const int grp_id = (int)((wgid & 7) * p.per_xcd + (r - bh * p.per_xcd));
+  if (bh >= p.BH || grp_id >= p.n_groups) return;   // uniform over the workgroup
+  const int qi0 = grp_id * p.G;
   const int nG = min(p.G, n_b - qi0);
 
   constexpr bool kBF = std::is_same<T, __bf16>::value;
@@ -590,7 +605,7 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedParams p) {
       for (int g = 0; g < kGMax; ++g) {
         if (g < nG) {
           const bool keep = (masks[g * n_words + (j >> 6)] >> (j & 63)) & 1ull;
-          const float wj = (keep || c2[g] == -INFINITY) ? 0.f : exp2f(shr[g][j] * kLog2e - c2[g]);
+          const float wj = (keep || c2[g] == -INFINITY) ? 0.f : fast_exp2(shr[g][j] * kLog2e - c2[g]);
           shr[g][j] = wj;
           lp[g] += wj;
         }
@@ -598,11 +613,16 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedParams p) {
     }
     block_sum_n<kGMax>(lp, misc);   // barrier: the weights are complete
     if (t < kGMax) misc[kL + t] = misc[kTot + t] * (float)kBlock;
-    constexpr int P = 256 / D;
-    const int col = t % D, part = t / D;
-    const float* vs = p.vsum + (size_t)bh * n_b * D + col;
-    float a[kGMax] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = part; j < n_b; j += P) {
+    // A_g = sum_j w_gj vsum_j: lane (jr, c4) takes columns 4*c4 .. 4*c4+3 of
+    // key blocks j = jr, jr + RG, ...; each float4 of vsum serves all G blocks
+    constexpr int C4 = D / 4, RG = 256 / C4;
+    const int c4 = t % C4, jr = t / C4;
+    const float4* vs = reinterpret_cast<const float4*>(p.vsum + (size_t)bh * n_b * D) + c4;
+    f32x4 a[kGMax];
+#pragma unroll
+    for (int g = 0; g < kGMax; ++g) a[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int j = jr; j < n_b; j += RG) {
       float wj[kGMax];
       bool any = false;
 #pragma unroll
@@ -611,20 +631,31 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedParams p) {
         any |= wj[g] != 0.f;
       }
       if (any) {
-        const float x = vs[(size_t)j * D];
+        const float4 x = vs[(size_t)j * C4];
 #pragma unroll
-        for (int g = 0; g < kGMax; ++g) a[g] += wj[g] * x;
+        for (int g = 0; g < kGMax; ++g) {
+          a[g][0] += wj[g] * x.x; a[g][1] += wj[g] * x.y;
+          a[g][2] += wj[g] * x.z; a[g][3] += wj[g] * x.w;
+        }
       }
     }
+    // fold the row groups of a wave (lanes c4 + C4*r), then the 4 waves via LDS
 #pragma unroll
-    for (int g = 0; g < kGMax; ++g) acc[(part * kGMax + g) * D + col] = a[g];
+    for (int o = C4; o < 64; o <<= 1)
+#pragma unroll
+      for (int g = 0; g < kGMax; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[g][e] += __shfl_xor(a[g][e], o, 64);
+    if (lane < C4)
+#pragma unroll
+      for (int g = 0; g < kGMax; ++g)
+        *reinterpret_cast<f32x4*>(acc + (w * kGMax + g) * D + 4 * c4) = a[g];
     __syncthreads();
     if (t < D) {
 #pragma unroll
       for (int g = 0; g < kGMax; ++g) {
-        float s = 0.f;
-#pragma unroll
-        for (int q = 0; q < P; ++q) s += acc[(q * kGMax + g) * D + t];
+        const float s = (acc[(0 * kGMax + g) * D + t] + acc[(1 * kGMax + g) * D + t]) +
+                        (acc[(2 * kGMax + g) * D + t] + acc[(3 * kGMax + g) * D + t]);
         qa[t * kGMax + g] = s;   // q_bar is no longer needed: qa now holds A
       }
     }
@@ -694,11 +725,11 @@ hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
   p.vt = a.ws.vt;
   p.kbar_t = a.ws.kbar_t; p.vsum = a.ws.vsum; p.kmean = a.ws.kmean; p.kcov = a.ws.kcov;
   p.n_b = s.n_b; p.n_b_pad = s.n_b_pad; p.n_words = s.n_words;
-  p.G = g.G; p.n_groups = g.n_groups; p.items = g.items; p.per_xcd = g.per_xcd;
+  p.G = g.G; p.n_groups = g.n_groups; p.BH = s.BH(); p.per_xcd = g.per_xcd;
   p.N = s.N;
   p.beta = a.beta; p.beta_mode = a.beta_mode;
   p.kept_per_row = a.kept_per_row; p.mask_bits = a.mask_bits; p.tau_out = a.tau;
-  const dim3 grid((unsigned)(8 * g.per_xcd));
+  const dim3 grid((unsigned)(8 * g.per_xcd * s.BH()));
   if (a.correction) {
     auto k = fused_kernel<T, D, true>;
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
@@ -721,7 +752,7 @@ FusedGeom geom_impl(const Shape& s) {
   g.G = cap < 1 ? 0 : (cap < kGMax ? cap : kGMax);
   g.n_groups = g.G ? (s.n_b + g.G - 1) / g.G : 0;
   g.items = s.BH() * g.n_groups;
-  g.per_xcd = (g.items + 7) / 8;
+  g.per_xcd = (g.n_groups + 7) / 8;
   g.lds_bytes = L::bytes(g.G, s.n_words);
   return g;
 }

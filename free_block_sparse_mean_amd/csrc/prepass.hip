@@ -7,7 +7,8 @@
 //   m       = mean over j of k_bar_j
 //   C       = (1/n_b) sum_j k_bar_j k_bar_j^T - m m^T   (population covariance)
 // and, for bf16 inputs, a copy of V with every 64 x d block transposed to
-// d x 64 (the layout the fused pass stages for its P.V products).
+// d x 64, keys permuted within each group of 32 into the order the fused
+// pass feeds them to its P.V MFMA (one 16-byte LDS read per operand).
 // Sources: page "Sol-Attn: l'attenzione sparsa che sceglie al volo"
 // (paithon.it), section "Perche l'attenzione pesa tanto nei video" for the
 // 64-token block means, section "Una soglia per ogni riga" (last paragraph)
@@ -92,17 +93,20 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const T* __restrict__ k
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // output chunk (d, kc): keys kc*8 .. kc*8+7 of head dim d, 16 bytes;
-    // consecutive lanes take consecutive d so the LDS column reads do not
-    // collide in banks
+    // Output chunk (d, kc) is 8 bf16 of head dim d: keys k0..k0+3 then
+    // k0+16..k0+19 with k0 = 32*(kc/4) + 4*(kc%4), the order in which a lane
+    // of the fused kernel holds P for one 16x16x32 MFMA k-step. Consecutive
+    // lanes take consecutive d, so the LDS column reads do not share banks.
     __bf16* dst = vt + ((size_t)bh * n_b + j) * D * 64;
     for (int c = lane; c < D * 8; c += 64) {
       const int d = c % D, kc = c / D;
+      const int k0 = 32 * (kc >> 2) + 4 * (kc & 3);
       uint32_t w[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const uint32_t lo = __builtin_bit_cast(unsigned short, stage[wv][(kc * 8 + 2 * h) * kPitch + d]);
-        const uint32_t hi = __builtin_bit_cast(unsigned short, stage[wv][(kc * 8 + 2 * h + 1) * kPitch + d]);
+        const int ka = k0 + (h >> 1) * 16 + 2 * (h & 1);
+        const uint32_t lo = __builtin_bit_cast(unsigned short, stage[wv][ka * kPitch + d]);
+        const uint32_t hi = __builtin_bit_cast(unsigned short, stage[wv][(ka + 1) * kPitch + d]);
         w[h] = lo | (hi << 16);
       }
       *reinterpret_cast<uint4*>(dst + (size_t)d * 64 + kc * 8) = make_uint4(w[0], w[1], w[2], w[3]);

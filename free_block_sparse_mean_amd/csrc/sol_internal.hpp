@@ -49,7 +49,7 @@ struct FusedGeom {
   int G;            // query blocks per workgroup
   int n_groups;     // ceil(n_b / G) per head
   long long items;  // BH * n_groups
-  long long per_xcd;  // ceil(items / 8)
+  long long per_xcd;  // ceil(n_groups / 8): work items of one head per XCD
   int lds_bytes;
 };
 FusedGeom fused_geom(const Shape& s, Dtype dt);

@@ -85,8 +85,10 @@ typedef struct sol_debug {
  *   vsum    [BH][n_b][d]  block sums of values (= 64 * v_bar_j)
  *   kmean   [BH][d]       m = mean over j of k_bar_j
  *   kcov    [BH][d][d]    C = (1/n_b) sum_j (k_bar_j - m)(k_bar_j - m)^T
- *   vt      [BH][n_b][d][64] bfloat16: each 64 x d block of V transposed
- *                         (written for bf16 inputs only)
+ *   vt      [BH][n_b][d][64] bfloat16: each 64 x d block of V transposed,
+ *                         column c holding key 32*(c/32) + 4*g + s for
+ *                         s = c%8 < 4, else 32*(c/32) + 16 + 4*g + s - 4,
+ *                         with g = (c%32)/8 (written for bf16 inputs only)
  * the remaining bytes are scratch of the pre-pass. */
 typedef struct sol_workspace_layout {
   size_t total_bytes;

@@ -143,8 +143,12 @@ def test_prepass_summaries(w, gpu_lib):
     torch.cuda.synchronize()
     raw = gpu_lib.workspace_views(ws, w.B, w.H, w.N, w.d)
     if w.dtype == BF:
-        # each 64 x d block of V transposed, bit for bit
-        vt_ref = v.view(w.B, w.H, w.n_blocks, 64, w.d).transpose(-1, -2)
+        # each 64 x d block of V transposed, bit for bit, keys in the documented order
+        c = torch.arange(64)
+        g, sl = (c % 32) // 8, c % 8
+        key = 32 * (c // 32) + torch.where(sl < 4, 4 * g + sl, 16 + 4 * g + sl - 4)
+        assert sorted(key.tolist()) == list(range(64))
+        vt_ref = v.view(w.B, w.H, w.n_blocks, 64, w.d).transpose(-1, -2)[..., key]
         assert torch.equal(raw["vt"].cpu(), vt_ref)
     views = {n: t.cpu().double().numpy() for n, t in raw.items() if n != "vt"}
     for b in range(w.B):

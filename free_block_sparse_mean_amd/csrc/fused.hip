@@ -168,23 +168,6 @@ __device__ inline void block_max_n(float (&x)[NV], float* misc) {
   __syncthreads();
 }
 
-struct Tile {
-  int g, j;   // query block within the group, key block; g < 0 when done
-};
-
-// Next kept (g, j) strictly after `cur` in (g, j) order, from the LDS masks.
-__device__ inline Tile next_tile(Tile cur, const uint64_t* masks, int nG, int n_words) {
-  int g = cur.g, j = cur.j + 1;
-  while (g < nG) {
-    const int wi = j >> 6;
-    if (wi >= n_words) { ++g; j = 0; continue; }
-    const uint64_t word = masks[g * n_words + wi] & (~0ull << (j & 63));
-    if (word) return Tile{g, wi * 64 + (int)__builtin_ctzll(word)};
-    j = (wi + 1) * 64;
-  }
-  return Tile{-1, 0};
-}
-
 // Per-lane state of the exact phase (one query row, a quarter of its keys / dims).
 template <typename T, int D> struct ExactState {
   static constexpr bool kBF = std::is_same<T, __bf16>::value;
@@ -199,15 +182,21 @@ template <typename T, int D> struct ExactState {
 };
 
 template <typename T, int D>
-__device__ __forceinline__ void reset_block(ExactState<T, D>& st, const T* Qr, int lane) {
+__device__ __forceinline__ void zero_state(ExactState<T, D>& st) {
   using S = ExactState<T, D>;
-  const int grp = lane >> 4;
   st.mrow = -INFINITY;
   st.lrow = 0.f;
 #pragma unroll
   for (int i = 0; i < S::NACC; ++i) st.oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < S::NF; ++i) st.of[i] = 0.f;
+}
+
+// this lane's part of its query row: MFMA operands (bf16) or D/4 floats (fp32)
+template <typename T, int D>
+__device__ __forceinline__ void load_q(ExactState<T, D>& st, const T* Qr, int lane) {
+  using S = ExactState<T, D>;
+  const int grp = lane >> 4;
   if constexpr (S::kBF) {
 #pragma unroll
     for (int ks = 0; ks < S::KS; ++ks) st.qop[ks] = *reinterpret_cast<const bf16x8*>(Qr + ks * 32 + grp * 8);
@@ -269,24 +258,39 @@ __device__ __forceinline__ void commit_f32(float* stK, float* stV, const float* 
   }
 }
 
+// Byte offsets of this lane's MFMA operand reads inside a tile buffer. The
+// swizzles depend on the row only through lane % 16 (every 16-row sub-tile
+// starts at a multiple of 16), so one offset per k-step serves all
+// sub-tiles, which differ by compile-time displacements.
+template <int D> struct LaneOfs {
+  int k[D / 32];   // K operand, k-step ks: row lane%16 of sub-tile 0, chunk 4ks + lane/16
+  int v[2];        // V^T operand, k-step ks: row lane%16 of d-tile 0, chunk 4ks + lane/16
+  __device__ __forceinline__ explicit LaneOfs(int lane) {
+    const int l16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) k[ks] = 16 * k_pos<D>(l16, ks * 4 + grp);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) v[ks] = Geom<__bf16, D>::kKBytes + 16 * v_pos(l16, ks * 4 + grp);
+  }
+};
+
 template <typename T, int D>
-__device__ __forceinline__ void compute_tile(ExactState<T, D>& st, const unsigned char* buf, int lane) {
+__device__ __forceinline__ void compute_tile(ExactState<T, D>& st, const unsigned char* buf, int lane,
+                                             const LaneOfs<D>& lo) {
   using S = ExactState<T, D>;
   using Gm = Geom<T, D>;
   constexpr float kScale2 = inv_sqrt(D) * kLog2e;   // logit -> base-2 exponent
   const int grp = lane >> 4;
   if constexpr (S::kBF) {
-    const unsigned char* bK = buf;
-    const unsigned char* bV = buf + Gm::kKBytes;
-    // S^T (64 keys x 16 queries of this wave): 4 key tiles of 16
+    // S^T (64 keys x 16 queries of this wave): 4 key tiles of 16 (16 rows of
+    // D/8 chunks = 16 * D * 2 bytes apart)
     f32x4 s[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            bK + 16 * k_pos<D>(kt * 16 + (lane & 15), ks * 4 + grp));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(buf + lo.k[ks] + kt * 16 * D * 2);
         s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, st.qop[ks], s[kt], 0, 0, 0);
       }
     }
@@ -326,8 +330,9 @@ __device__ __forceinline__ void compute_tile(ExactState<T, D>& st, const unsigne
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int dt = 0; dt < S::NACC; ++dt) {
-        // keys of k-step ks for this lane group, stored in operand order
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(bV + 16 * v_pos(dt * 16 + (lane & 15), ks * 4 + grp));
+        // keys of k-step ks for this lane group, stored in operand order;
+        // d-tiles are 16 rows of 8 chunks = 2048 bytes apart
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(buf + lo.v[ks] + dt * 2048);
         st.oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[ks], st.oacc[dt], 0, 0, 0);
       }
     }
@@ -414,7 +419,7 @@ __device__ __forceinline__ void epilogue(ExactState<T, D>& st, const FusedParams
 }
 
 template <typename T, int D, bool CORR>
-__global__ __launch_bounds__(256) void fused_kernel(FusedParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel(FusedParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   using Gm = Geom<T, D>;
   using L = Lds<T, D>;
@@ -663,56 +668,77 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedParams p) {
   __syncthreads();   // masks, A, L, c2 visible; the proxy rows are dead
 
   // ---- 5. inner loop: exact attention on the kept tiles ---------------------
-  ExactState<T, D> st;
   const int row = 16 * w + (lane & 15);   // this lane's query row within a block
-  int cg = 0;
-  reset_block<T, D>(st, Qh + ((size_t)qi0 * kBlock + row) * D, lane);
-  Tile cur = next_tile(Tile{0, -1}, masks, nG, n_words);
-  // finish every query block before block `upto` (no kept tiles left for them)
-#define SOL_FINISH_BEFORE(upto)                                                   \
-  while (cg < (upto)) {                                                           \
-    epilogue<T, D>(st, p, bh, qi0 + cg, cg, row, lane, qa, misc);                 \
-    ++cg;                                                                         \
-    reset_block<T, D>(st, Qh + ((size_t)(qi0 + cg) * kBlock + row) * D, lane);    \
-  }
+  const LaneOfs<D> lofs(lane);
   if constexpr (kBF) {
-    // one barrier per tile: wait for this lane's loads of `cur`, barrier (all
-    // lanes' loads landed; every wave finished the previous tile, so the other
-    // buffer is free), start loading `nxt` into it, compute `cur`
+    // The G blocks' kept lists are walked together in ascending key-block
+    // order: each tile of their union is loaded once and computed for every
+    // block that keeps it; the G online-softmax states stay in registers.
+    // One barrier per union tile: wait for this lane's loads of tile j,
+    // barrier (all lanes' loads landed; every wave finished the previous tile,
+    // so the other buffer is free), start loading the next union tile into
+    // it, compute tile j.
+    ExactState<T, D> sts[kGMax];
+#pragma unroll
+    for (int g = 0; g < kGMax; ++g) {
+      zero_state<T, D>(sts[g]);
+      if (g < nG) load_q<T, D>(sts[g], Qh + ((size_t)(qi0 + g) * kBlock + row) * D, lane);
+    }
+    auto union_next = [&](int j) -> int {   // next key block after j kept by any block
+      for (int wi = (j + 1) >> 6; wi < n_words; ++wi) {
+        uint64_t word = 0;
+#pragma unroll
+        for (int g = 0; g < kGMax; ++g)
+          if (g < nG) word |= masks[g * n_words + wi];
+        if (wi == ((j + 1) >> 6)) word &= ~0ull << ((j + 1) & 63);
+        if (word) return wi * 64 + (int)__builtin_ctzll(word);
+      }
+      return -1;
+    };
 #define SOL_STEP(CURB, NEXTB)                                                     \
     {                                                                             \
-      SOL_FINISH_BEFORE(cur.g)                                                    \
-      const Tile nxt = next_tile(cur, masks, nG, n_words);                        \
+      unsigned keep = 0;                                                          \
+      _Pragma("unroll") for (int g = 0; g < kGMax; ++g)                           \
+        if (g < nG) keep |= (unsigned)((masks[g * n_words + (j >> 6)] >> (j & 63)) & 1ull) << g; \
+      const int nj = union_next(j);                                               \
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                           \
       __syncthreads();                                                            \
-      if (nxt.g >= 0) issue_tile<D>(NEXTB, Kh, p.vt, bh, n_b, nxt.j, t);          \
-      compute_tile<T, D>(st, CURB, lane);                                         \
-      cur = nxt;                                                                  \
+      if (nj >= 0) issue_tile<D>(NEXTB, Kh, p.vt, bh, n_b, nj, t);                \
+      _Pragma("unroll") for (int g = 0; g < kGMax; ++g)                           \
+        if (keep & (1u << g)) compute_tile<T, D>(sts[g], CURB, lane, lofs);       \
+      j = nj;                                                                     \
     }
-    if (cur.g >= 0) issue_tile<D>(sbufA, Kh, p.vt, bh, n_b, cur.j, t);
-    while (cur.g >= 0) {
+    int j = union_next(-1);
+    if (j >= 0) issue_tile<D>(sbufA, Kh, p.vt, bh, n_b, j, t);
+    while (j >= 0) {
       SOL_STEP(sbufA, sbufB)
-      if (cur.g < 0) break;
+      if (j < 0) break;
       SOL_STEP(sbufB, sbufA)
     }
 #undef SOL_STEP
+#pragma unroll
+    for (int g = 0; g < kGMax; ++g)
+      if (g < nG) epilogue<T, D>(sts[g], p, bh, qi0 + g, g, row, lane, qa, misc);
   } else {
-    while (cur.g >= 0) {
-      SOL_FINISH_BEFORE(cur.g)
-      const Tile nxt = next_tile(cur, masks, nG, n_words);
-      __syncthreads();
-      commit_f32<D>(reinterpret_cast<float*>(sbufA), reinterpret_cast<float*>(sbufA + Gm::kKBytes),
-                    reinterpret_cast<const float*>(Kh), reinterpret_cast<const float*>(Vh), cur.j, t);
-      __syncthreads();
-      compute_tile<T, D>(st, sbufA, lane);
-      cur = nxt;
+    // fp32: the blocks one after another, one tile at a time
+    ExactState<T, D> st;
+    for (int g = 0; g < nG; ++g) {
+      zero_state<T, D>(st);
+      load_q<T, D>(st, Qh + ((size_t)(qi0 + g) * kBlock + row) * D, lane);
+      for (int wi = 0; wi < n_words; ++wi) {
+        uint64_t word = masks[g * n_words + wi];
+        while (word) {
+          const int j = wi * 64 + (int)__builtin_ctzll(word);
+          word &= word - 1;
+          __syncthreads();
+          commit_f32<D>(reinterpret_cast<float*>(sbufA), reinterpret_cast<float*>(sbufA + Gm::kKBytes),
+                        reinterpret_cast<const float*>(Kh), reinterpret_cast<const float*>(Vh), j, t);
+          __syncthreads();
+          compute_tile<T, D>(st, sbufA, lane, lofs);
+        }
+      }
+      epilogue<T, D>(st, p, bh, qi0 + g, g, row, lane, qa, misc);
     }
-  }
-#undef SOL_FINISH_BEFORE
-  while (cg < nG) {
-    epilogue<T, D>(st, p, bh, qi0 + cg, cg, row, lane, qa, misc);
-    ++cg;
-    if (cg < nG) reset_block<T, D>(st, Qh + ((size_t)(qi0 + cg) * kBlock + row) * D, lane);
   }
 }
 

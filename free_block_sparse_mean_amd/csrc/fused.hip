@@ -104,17 +104,15 @@ template <int D> __device__ __forceinline__ int k_pos(int r, int c) {
 // LDS position of chunk kc (keys 8kc .. 8kc+7) of row d of a V^T tile.
 __device__ __forceinline__ int v_pos(int d, int kc) { return d * 8 + (kc ^ ((d >> 1) & 7)); }
 
-__host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
 
 // LDS map. Static: two tile buffers A and B (separate objects, so the compiler
 // can see that loads into one do not alias reads of the other); during
-// routing they hold the G proxy rows (rows_per_buf rows each). Dynamic:
-// [masks | qa | acc | misc].
+// routing they hold the G proxy rows (rows_per_buf rows each); the kept-set
+// words are a third static object. Dynamic: [qa | acc | misc].
 template <typename T, int D> struct Lds {
   static constexpr int kBuf = Geom<T, D>::kBufBytes;
   __host__ __device__ static int rows_per_buf(int nbp) { return kBuf / (4 * nbp); }
-  __host__ __device__ static int masks() { return 0; }
-  __host__ __device__ static int qa(int G, int nw) { return align16(8 * G * nw); }
+  __host__ __device__ static int qa(int, int) { return 0; }
   __host__ __device__ static int acc(int G, int nw) { return qa(G, nw) + 4 * D * kGMax; }
   __host__ __device__ static int misc(int G, int nw) { return acc(G, nw) + 4 * 4 * D * kGMax; }
   __host__ __device__ static int bytes(int G, int nw) { return misc(G, nw) + 4 * 64; }
@@ -212,33 +210,51 @@ __device__ __forceinline__ void load_q(ExactState<T, D>& st, const T* Qr, int la
 typedef __attribute__((address_space(3))) void lds_ptr_t;
 typedef __attribute__((address_space(1))) const void gbl_ptr_t;
 
+// Per-lane pieces of the tile loads. A tile region (K or V^T, 64 * D * 2
+// bytes) is moved in slabs of 256 chunks of 16 bytes, one chunk per lane; the
+// lane's source offset inside a slab is the same for every slab (the XOR
+// swizzles depend on the row only through bits that do not change between
+// slabs), slabs are 4096 bytes apart in both global memory and LDS, and the
+// LDS destination of a wave is uniform (kept in a scalar register).
+struct DmaLane {
+  int k_off;      // byte offset of this lane's K chunk in slab 0 of the tile
+  int v_off;      // byte offset of this lane's V^T chunk in slab 0
+  int wave_lds;   // this wave's first LDS byte inside a slab (uniform)
+};
+template <int D>
+__device__ __forceinline__ DmaLane dma_lane(int t) {
+  DmaLane dl;
+  if constexpr (D == 128) {
+    const int r = t >> 4, c = (t & 15) ^ (r & 15);          // rows of 16 chunks
+    dl.k_off = r * D * 2 + c * 16;
+  } else {
+    const int r = t >> 3, c = (t & 7) ^ ((r >> 1) & 7);     // rows of 8 chunks
+    dl.k_off = r * D * 2 + c * 16;
+  }
+  const int d = t >> 3, kc = (t & 7) ^ ((d >> 1) & 7);      // V^T rows of 8 chunks
+  dl.v_off = d * 128 + kc * 16;
+  dl.wave_lds = __builtin_amdgcn_readfirstlane((t >> 6) * 1024);
+  return dl;
+}
+
 // bf16: start loading the K tile and the transposed V tile of key block j
-// straight into LDS buffer `buf` (each lane moves D/32 chunks of each).
-// Completion is awaited with s_waitcnt vmcnt(0) before the next barrier.
+// straight into LDS buffer `buf`. Completion is awaited with s_waitcnt vmcnt
+// before the next barrier.
 template <int D>
 __device__ __forceinline__ void issue_tile(unsigned char* buf, const __bf16* Kh, const __bf16* Vt,
-                                           long long bh, int n_b, int j, int t) {
-  constexpr int NI = D / 32;   // instructions per lane for each of K and V^T
-  const __bf16* Kj = Kh + (size_t)j * kBlock * D;
-  const __bf16* Vj = Vt + ((size_t)bh * n_b + j) * D * 64;
-  const int wbase = t & ~63;   // first chunk of this wave in each 256-chunk slab
+                                           long long bh, int n_b, int j, const DmaLane& dl) {
+  constexpr int NI = D / 32;   // slabs per region
+  const unsigned char* Kj = reinterpret_cast<const unsigned char*>(Kh + (size_t)j * kBlock * D);
+  const unsigned char* Vj = reinterpret_cast<const unsigned char*>(Vt + ((size_t)bh * n_b + j) * D * 64);
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int q = i * 256 + t;                  // LDS chunk this lane fills
-    const int r = q / (D / 8), pc = q % (D / 8);
-    const int c = pc ^ (D == 128 ? (r & 15) : ((r >> 1) & 7));
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(Kj + r * D + c * 8),
-                                     (lds_ptr_t*)(buf + (i * 256 + wbase) * 16), 16, 0, 0);
-  }
+  for (int i = 0; i < NI; ++i)
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(Kj + dl.k_off + i * 4096),
+                                     (lds_ptr_t*)(buf + i * 4096 + dl.wave_lds), 16, 0, 0);
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int q = i * 256 + t;
-    const int d = q >> 3, pc = q & 7;
-    const int kc = pc ^ ((d >> 1) & 7);
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(Vj + d * 64 + kc * 8),
-                                     (lds_ptr_t*)(buf + Geom<__bf16, D>::kKBytes + (i * 256 + wbase) * 16),
+  for (int i = 0; i < NI; ++i)
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(Vj + dl.v_off + i * 4096),
+                                     (lds_ptr_t*)(buf + Geom<__bf16, D>::kKBytes + i * 4096 + dl.wave_lds),
                                      16, 0, 0);
-  }
 }
 
 // fp32: stage the K and V tiles of key block j in LDS (synchronously)
@@ -444,7 +460,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr bool kBF = std::is_same<T, __bf16>::value;
   __shared__ __attribute__((aligned(16))) unsigned char sbufA[Gm::kBufBytes];
   __shared__ __attribute__((aligned(16))) unsigned char sbufB[Gm::kBuffers == 2 ? Gm::kBufBytes : 16];
-  uint64_t* masks = reinterpret_cast<uint64_t*>(lds + L::masks());          // [G][n_words]
+  // kept-set words [G][n_words]: a static object of its own, so the compiler
+  // sees that the LDS-DMA loads in flight do not write them
+  __shared__ uint64_t masks[kGMax * (kMaxBlocks / 64)];
   float* qa = reinterpret_cast<float*>(lds + L::qa(p.G, n_words));          // [D][kGMax]
   float* acc = reinterpret_cast<float*>(lds + L::acc(p.G, n_words));        // [4][kGMax][D]
   float* misc = reinterpret_cast<float*>(lds + L::misc(p.G, n_words));
@@ -678,6 +696,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // barrier (all lanes' loads landed; every wave finished the previous tile,
     // so the other buffer is free), start loading the next union tile into
     // it, compute tile j.
+    const DmaLane dl = dma_lane<D>(t);
     ExactState<T, D> sts[kGMax];
 #pragma unroll
     for (int g = 0; g < kGMax; ++g) {
@@ -695,27 +714,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       return -1;
     };
+// s_waitcnt vmcnt(0) through the builtin, so the compiler's own wait tracking
+// knows the tile loads have landed (gfx9 encoding: vmcnt in bits 3:0, expcnt
+// 6:4 and lgkmcnt 11:8 left at their maxima)
+#define SOL_WAIT_VM() __builtin_amdgcn_s_waitcnt(0xF70)
 #define SOL_STEP(CURB, NEXTB)                                                     \
     {                                                                             \
       unsigned keep = 0;                                                          \
       _Pragma("unroll") for (int g = 0; g < kGMax; ++g)                           \
         if (g < nG) keep |= (unsigned)((masks[g * n_words + (j >> 6)] >> (j & 63)) & 1ull) << g; \
       const int nj = union_next(j);                                               \
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                           \
-      __syncthreads();                                                            \
-      if (nj >= 0) issue_tile<D>(NEXTB, Kh, p.vt, bh, n_b, nj, t);                \
+      /* this lane's loads of tile j have landed; the tile loop writes LDS  */    \
+      /* only through those loads and every read of the other buffer was    */    \
+      /* consumed by an MFMA, so a bare barrier suffices                    */    \
+      SOL_WAIT_VM();                                                              \
+      asm volatile("" ::: "memory");                                              \
+      __builtin_amdgcn_s_barrier();                                               \
+      asm volatile("" ::: "memory");                                              \
+      if (nj >= 0) issue_tile<D>(NEXTB, Kh, p.vt, bh, n_b, nj, dl);               \
       _Pragma("unroll") for (int g = 0; g < kGMax; ++g)                           \
         if (keep & (1u << g)) compute_tile<T, D>(sts[g], CURB, lane, lofs);       \
       j = nj;                                                                     \
     }
     int j = union_next(-1);
-    if (j >= 0) issue_tile<D>(sbufA, Kh, p.vt, bh, n_b, j, t);
+    if (j >= 0) issue_tile<D>(sbufA, Kh, p.vt, bh, n_b, j, dl);
     while (j >= 0) {
       SOL_STEP(sbufA, sbufB)
       if (j < 0) break;
       SOL_STEP(sbufB, sbufA)
     }
 #undef SOL_STEP
+#undef SOL_WAIT_VM
+    // no LDS load may land after the workgroup has released its LDS
+    __builtin_amdgcn_s_waitcnt(0xF70);
 #pragma unroll
     for (int g = 0; g < kGMax; ++g)
       if (g < nG) epilogue<T, D>(sts[g], p, bh, qi0 + g, g, row, lane, qa, misc);

@@ -526,6 +526,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int P = 256 / D;
     const int r = t % D, part = t / D;
     float y[kGMax] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
     for (int c = part; c < D; c += P) {
       const float cv = C[(size_t)c * D + r];
       const float4 qv = *reinterpret_cast<const float4*>(qa + c * kGMax);
@@ -557,7 +558,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int g = 0; g < kGMax; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) a[g][e] = 0.f;
-#pragma unroll 8
+#pragma unroll 16
       for (int c = 0; c < D; ++c) {
         const float4 kv = *reinterpret_cast<const float4*>(kt + (size_t)c * nbp + j4);
         const float4 qv = *reinterpret_cast<const float4*>(qa + c * kGMax);
@@ -644,22 +645,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x4 a[kGMax];
 #pragma unroll
     for (int g = 0; g < kGMax; ++g) a[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
+    // unconditional loads (kept blocks carry weight 0), so the unrolled
+    // iterations keep several L2 loads in flight
+#pragma unroll 8
     for (int j = jr; j < n_b; j += RG) {
-      float wj[kGMax];
-      bool any = false;
+      const float4 x = vs[(size_t)j * C4];
 #pragma unroll
       for (int g = 0; g < kGMax; ++g) {
-        wj[g] = g < nG ? shr[g][j] : 0.f;
-        any |= wj[g] != 0.f;
-      }
-      if (any) {
-        const float4 x = vs[(size_t)j * C4];
-#pragma unroll
-        for (int g = 0; g < kGMax; ++g) {
-          a[g][0] += wj[g] * x.x; a[g][1] += wj[g] * x.y;
-          a[g][2] += wj[g] * x.z; a[g][3] += wj[g] * x.w;
-        }
+        const float wj = g < nG ? shr[g][j] : 0.f;
+        a[g][0] += wj * x.x; a[g][1] += wj * x.y;
+        a[g][2] += wj * x.z; a[g][3] += wj * x.w;
       }
     }
     // fold the row groups of a wave (lanes c4 + C4*r), then the 4 waves via LDS

@@ -45,6 +45,24 @@ __device__ inline float wave_max(float x) {
   return x;
 }
 
+// Reductions over the 4 lanes {l, l^16, l^32, l^48} (lanes that share l % 16)
+// with the gfx950 permlane swaps: permlane16_swap(x, x) returns, in some
+// order, the values of lane l and lane l^16, permlane32_swap those of l and
+// l^32, so one VALU op per step replaces an LDS shuffle; both lanes of a pair
+// combine the same two values in the same order, so they agree bit for bit.
+__device__ inline float quad16_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float quad16_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // float -> bfloat16, round to nearest even (finite inputs)
 __device__ inline __bf16 to_bf16(float f) { return (__bf16)f; }
 

@@ -316,9 +316,7 @@ __device__ __forceinline__ void compute_tile(ExactState<T, D>& st, const unsigne
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[kt][i]);
-    tmax *= kScale2;
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = quad16_max(tmax) * kScale2;
     // move the reference only when the tile maximum exceeds it by the slack
     const bool grow = tmax > st.mrow + kRescaleSlack;
     if (__ballot(grow)) {
@@ -394,10 +392,7 @@ __device__ __forceinline__ void epilogue(ExactState<T, D>& st, const FusedParams
   using S = ExactState<T, D>;
   const int grp = lane >> 4;
   float l = st.lrow;
-  if constexpr (S::kBF) {
-    l += __shfl_xor(l, 16, 64);   // lanes of one row held partial key sums
-    l += __shfl_xor(l, 32, 64);
-  }
+  if constexpr (S::kBF) l = quad16_sum(l);   // lanes of one row held partial key sums
   const float c2 = misc[kC2 + g], Lg = misc[kL + g];
   const float M = fmaxf(st.mrow, c2);
   const float fo = (st.mrow == -INFINITY) ? 0.f : fast_exp2(st.mrow - M);

@@ -290,70 +290,97 @@ template <int D> struct LaneOfs {
   }
 };
 
-template <typename T, int D>
-__device__ __forceinline__ void compute_tile(ExactState<T, D>& st, const unsigned char* buf, int lane,
-                                             const LaneOfs<D>& lo) {
-  using S = ExactState<T, D>;
-  using Gm = Geom<T, D>;
+// One tile of 64 keys for one query block of this wave: S^T = K Q^T, online
+// softmax in base 2, O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void tile_bf16(ExactState<__bf16, D>& st, const unsigned char* buf, const LaneOfs<D>& lo) {
+  using S = ExactState<__bf16, D>;
+  constexpr float kScale2 = inv_sqrt(D) * kLog2e;   // logit -> base-2 exponent
+  // S^T (64 keys x 16 queries): 4 key sub-tiles of 16 rows of D/8 chunks
+  // (16*D*2 bytes apart). K-step outer, sub-tile inner: four independent
+  // accumulation chains, and the operands of k-step ks+1 are read while the
+  // MFMAs of k-step ks run.
+  f32x4 s[4];
+  bf16x8 ka[2][4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ka[0][kt] = *reinterpret_cast<const bf16x8*>(buf + lo.k[0] + kt * 16 * D * 2);
+  }
+#pragma unroll
+  for (int ks = 0; ks < S::KS; ++ks) {
+    if (ks + 1 < S::KS) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        ka[(ks + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(buf + lo.k[ks + 1] + kt * 16 * D * 2);
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks & 1][kt], st.qop[ks], s[kt], 0, 0, 0);
+  }
+  // Online softmax: the lane holds keys 16kt + (lane/16)*4 + i of its query
+  // row. A row's reference moves only when the tile maximum exceeds it by the
+  // slack. Each lane first tests its own 16 values; only when some lane of
+  // the wave passes are the four lanes of each row reconciled (row maximum
+  // over the tile, the same on the row's four lanes, so they stay in step).
+  float lmax = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, s[kt][i]);
+  lmax *= kScale2;
+  if (__ballot(lmax > st.mrow + kRescaleSlack)) {
+    const float tmax = quad16_max(lmax);
+    const bool grow = tmax > st.mrow + kRescaleSlack;
+    const float mnew = grow ? tmax : st.mrow;
+    const float alpha = fast_exp2(st.mrow - mnew);   // 0 on the first tile, 1 if !grow
+    st.lrow *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < S::NACC; ++dt) st.oacc[dt] *= alpha;
+    st.mrow = mnew;
+  }
+  const float mref = st.mrow;
+  bf16x8 pop[2];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pop[kt >> 1][(kt & 1) * 4 + i] = to_bf16(fast_exp2(__builtin_fmaf(s[kt][i], kScale2, -mref)));
+  // the row sum adds the bf16 weights that enter the P V product, two per
+  // dot2 instruction (products by 1 are exact, accumulation in fp32)
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float l = st.lrow;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+      l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pop[ks][e], pop[ks][e + 1]}, ones, l, false);
+  st.lrow = l;
+  // O^T (d x 16 queries) += V^T (d x 64 keys) P^T in two k-steps of 32 keys;
+  // V^T columns are stored in operand order; d-tiles are 16 rows of 8 chunks
+  // = 2048 bytes apart
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int dt = 0; dt < S::NACC; ++dt) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(buf + lo.v[ks] + dt * 2048);
+      st.oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[ks], st.oacc[dt], 0, 0, 0);
+    }
+  }
+}
+
+// One tile of 64 keys for one query block, fp32: 4 lanes per query row, each
+// a quarter of the head dims; dot products and the weighted sum of V on the
+// VALU from LDS-staged K and V; online softmax in base 2.
+template <int D>
+__device__ __forceinline__ void tile_f32(ExactState<float, D>& st, const unsigned char* buf, int lane) {
+  using S = ExactState<float, D>;
+  using Gm = Geom<float, D>;
   constexpr float kScale2 = inv_sqrt(D) * kLog2e;   // logit -> base-2 exponent
   const int grp = lane >> 4;
-  if constexpr (S::kBF) {
-    // S^T (64 keys x 16 queries of this wave): 4 key tiles of 16 (16 rows of
-    // D/8 chunks = 16 * D * 2 bytes apart)
-    f32x4 s[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(buf + lo.k[ks] + kt * 16 * D * 2);
-        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, st.qop[ks], s[kt], 0, 0, 0);
-      }
-    }
-    // online softmax (base 2): lane holds keys kt*16 + grp*4 + i of its query row
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[kt][i]);
-    tmax = quad16_max(tmax) * kScale2;
-    // move the reference only when the tile maximum exceeds it by the slack
-    const bool grow = tmax > st.mrow + kRescaleSlack;
-    if (__ballot(grow)) {
-      const float mnew = grow ? tmax : st.mrow;
-      const float alpha = fast_exp2(st.mrow - mnew);   // 0 on the first tile, 1 if !grow
-      st.lrow *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < S::NACC; ++dt) st.oacc[dt] *= alpha;
-      st.mrow = mnew;
-    }
-    const float mref = st.mrow;
-    float psum = 0.f;
-    bf16x8 pop[2];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pvv = fast_exp2(__builtin_fmaf(s[kt][i], kScale2, -mref));
-        psum += pvv;
-        pop[kt >> 1][(kt & 1) * 4 + i] = to_bf16(pvv);
-      }
-    st.lrow += psum;
-    // O^T (d x 16 queries) += V^T (d x 64 keys) P^T: two k-steps of 32 keys
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int dt = 0; dt < S::NACC; ++dt) {
-        // keys of k-step ks for this lane group, stored in operand order;
-        // d-tiles are 16 rows of 8 chunks = 2048 bytes apart
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(buf + lo.v[ks] + dt * 2048);
-        st.oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[ks], st.oacc[dt], 0, 0, 0);
-      }
-    }
-  } else {
+  {
     const float* stK = reinterpret_cast<const float*>(buf);
     const float* stV = reinterpret_cast<const float*>(buf + Gm::kKBytes);
-    // fp32: 4 lanes per query row, each a quarter of the head dims
     float sv[64];
     float tmax = -INFINITY;
 #pragma unroll
@@ -677,7 +704,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---- 5. inner loop: exact attention on the kept tiles ---------------------
   const int row = 16 * w + (lane & 15);   // this lane's query row within a block
-  const LaneOfs<D> lofs(lane);
   if constexpr (kBF) {
     // The G blocks' kept lists are walked together in ascending key-block
     // order: each tile of their union is loaded once and computed for every
@@ -686,6 +712,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // barrier (all lanes' loads landed; every wave finished the previous tile,
     // so the other buffer is free), start loading the next union tile into
     // it, compute tile j.
+    const LaneOfs<D> lofs(lane);
     const DmaLane dl = dma_lane<D>(t);
     ExactState<T, D> sts[kGMax];
 #pragma unroll
@@ -722,8 +749,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       __builtin_amdgcn_s_barrier();                                               \
       asm volatile("" ::: "memory");                                              \
       if (nj >= 0) issue_tile<D>(NEXTB, Kh, p.vt, bh, n_b, nj, dl);               \
-      _Pragma("unroll") for (int g = 0; g < kGMax; ++g)                           \
-        if (keep & (1u << g)) compute_tile<T, D>(sts[g], CURB, lane, lofs);       \
+      _Pragma("unroll") for (int g = 0; g < kGMax; ++g)                          \
+        if (keep & (1u << g)) tile_bf16<D>(sts[g], CURB, lofs);                   \
       j = nj;                                                                     \
     }
     int j = union_next(-1);
@@ -755,7 +782,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           commit_f32<D>(reinterpret_cast<float*>(sbufA), reinterpret_cast<float*>(sbufA + Gm::kKBytes),
                         reinterpret_cast<const float*>(Kh), reinterpret_cast<const float*>(Vh), j, t);
           __syncthreads();
-          compute_tile<T, D>(st, sbufA, lane, lofs);
+          tile_f32<D>(st, sbufA, lane);
         }
       }
       epilogue<T, D>(st, p, bh, qi0 + g, g, row, lane, qa, misc);

@@ -127,7 +127,7 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true", help="skip timing the dense path")
     ap.add_argument("--no-correction", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-blocks-per-head", type=int, default=8)
+    ap.add_argument("--cpu-blocks-per-head", type=int, default=128)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (for counter scaling)")
     args = ap.parse_args()

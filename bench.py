@@ -21,6 +21,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -60,7 +61,8 @@ def traffic_from_profile():
 
 
 def time_steps(fn_pre, fn_fused, steps: int):
-    """Time `steps` steps on the current stream; returns (ms/step, fused ms, prepass ms, wall s)."""
+    """Time `steps` steps on the current stream; returns (ms/step, mean fused ms, prepass ms,
+    wall s, fused ms of each step)."""
     import torch
     st = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -80,9 +82,9 @@ def time_steps(fn_pre, fn_fused, steps: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
-    fused = sum(fa[i].elapsed_time(fb[i]) for i in range(steps)) / steps
+    fused_each = [fa[i].elapsed_time(fb[i]) for i in range(steps)]
     pre = sum(pa[i].elapsed_time(pb[i]) for i in range(steps)) / steps
-    return ms, fused, pre, wall
+    return ms, sum(fused_each) / steps, pre, wall, fused_each
 
 
 def cpu_baseline(w, q, k, v, beta: float, blocks_per_head: int, heads):
@@ -108,6 +110,7 @@ def cpu_baseline(w, q, k, v, beta: float, blocks_per_head: int, heads):
     tflops = n_blocks * per_block / el / 1e12
     return {
         "value": tflops, "unit": "TFLOP/s (dense-equivalent)", "cores": int(cores), "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"{blocks_per_head} seeded query blocks x {len(heads)} heads of the "
                    f"{w.name} workload (B={w.B}, H={w.H}, N={w.N}, d={w.d}), beta={beta}, "
                    f"correction on: {n_blocks} of {w.B * w.H * nb} query blocks"),
@@ -116,14 +119,57 @@ def cpu_baseline(w, q, k, v, beta: float, blocks_per_head: int, heads):
     }
 
 
+def row_stats(kept) -> dict:
+    """Kept key blocks per query block (row of blocks) of the last stats call: histogram in
+    bins of 8, max/mean, p99/mean and coefficient of variation."""
+    import numpy as np
+    x = kept.flatten().cpu().numpy().astype(np.float64)
+    mean = float(x.mean())
+    hist, edges = np.histogram(x, bins=np.arange(0, x.max() + 9, 8))
+    return {"mean": mean, "max_over_mean": float(x.max() / mean) if mean else None,
+            "p99_over_mean": float(np.percentile(x, 99) / mean) if mean else None,
+            "cv": float(x.std() / mean) if mean else None, "min": int(x.min()), "max": int(x.max()),
+            "hist_bin": 8, "hist": hist.tolist()}
+
+
+def load_balance(sb, qd, kd, vd, out, ws, beta, flags, w) -> dict:
+    """One untimed fused call that records each workgroup's start and end on the device's
+    100 MHz clock: spread (max - min) / mean of the per-work-item busy times."""
+    import numpy as np
+    import torch
+    nb = w.n_blocks
+    clk = torch.zeros((w.B * w.H * nb, 2), dtype=torch.int64, device=qd.device)
+    sb.sol_block_summaries(kd, vd, ws)
+    sb.sol_attn_fused(qd, kd, vd, out, beta, flags, ws, item_clock=clk)
+    torch.cuda.synchronize()
+    c = clk.cpu().numpy()
+    c = c[c[:, 0] != 0].astype(np.float64)
+    busy = (c[:, 1] - c[:, 0]) * 0.01   # microseconds
+    span = (c[:, 1].max() - c[:, 0].min()) * 0.01
+    m = float(busy.mean())
+    return {"work_items": int(len(busy)), "busy_us_mean": m, "busy_us_min": float(busy.min()),
+            "busy_us_max": float(busy.max()), "spread": float((busy.max() - busy.min()) / m),
+            "p99_over_mean": float(np.percentile(busy, 99) / m), "launch_span_us": float(span)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4_stress_128k")
     ap.add_argument("--beta", type=float, default=1.5, help="headline beta")
-    ap.add_argument("--extra-betas", default="2.0", help="comma list, '' for none")
+    ap.add_argument("--extra-betas", default="1.645,2.0", help="comma list, '' for none")
     ap.add_argument("--no-dense", action="store_true", help="skip timing the dense path")
     ap.add_argument("--no-correction", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -181,11 +227,12 @@ def main() -> int:
         pre, fused = stepper(beta, flags)
         for _ in range(warmup):
             pre(); fused()
-        ms, fused_ms, pre_ms, wall = time_steps(pre, fused, steps)
+        ms, fused_ms, pre_ms, wall, each = time_steps(pre, fused, steps)
         kf = kept_flop(w, n_kept)
         return {
             "beta": beta if math.isfinite(beta) else str(beta),
             "ms": ms, "fused_ms": fused_ms, "prepass_ms": pre_ms, "wall_s": wall,
+            "fused_ms_median": statistics.median(each), "fused_ms_min": min(each), "reps": steps,
             "dense_equiv_tflops": dense_equiv_flop(w) / (ms * 1e-3) / 1e12,
             "density": n_kept / (w.B * w.H * nb * nb),
             "kept_blocks": n_kept,
@@ -195,6 +242,8 @@ def main() -> int:
         }
 
     head = measure(args.beta, corr, args.steps, args.warmup)
+    rows = row_stats(kept)
+    balance = load_balance(sb, qd, kd, vd, out, ws, args.beta, corr, w)
     # the two-call step equals one sol_attn_fwd_ex call (bit for bit)
     ref = out.clone()
     sb.sol_attn_fwd_ex(qd, kd, vd, out, args.beta, corr, workspace=ws)
@@ -244,6 +293,8 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_beta": per_beta,
+        "kept_per_row": rows,
+        "load_balance": balance,
         "prepass": {"ms": head["prepass_ms"], "hbm_gbs": head["prepass_hbm_gbs"],
                     "frac": head["prepass_hbm_gbs"] / PEAK_HBM_GBS},
         "checks": {"two_call_step_equals_fwd_ex": same_as_fwd_ex},

@@ -42,7 +42,8 @@ class SolError(RuntimeError):
 class sol_debug(ctypes.Structure):
     _fields_ = [("kept_per_row", ctypes.c_void_p),
                 ("mask_bits", ctypes.c_void_p),
-                ("tau", ctypes.c_void_p)]
+                ("tau", ctypes.c_void_p),
+                ("item_clock", ctypes.c_void_p)]
 
 
 class sol_workspace_layout(ctypes.Structure):
@@ -134,11 +135,11 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _dbg(kept_per_row=None, mask_bits=None, tau=None):
-    if kept_per_row is None and mask_bits is None and tau is None:
+def _dbg(kept_per_row=None, mask_bits=None, tau=None, item_clock=None):
+    if kept_per_row is None and mask_bits is None and tau is None and item_clock is None:
         return None
     ptr = lambda t: None if t is None else t.data_ptr()
-    return ctypes.byref(sol_debug(ptr(kept_per_row), ptr(mask_bits), ptr(tau)))
+    return ctypes.byref(sol_debug(ptr(kept_per_row), ptr(mask_bits), ptr(tau), ptr(item_clock)))
 
 
 def new_workspace(B: int, H: int, N: int, d: int, device=None) -> torch.Tensor:
@@ -176,19 +177,19 @@ def sol_block_summaries(k: torch.Tensor, v: torch.Tensor, workspace: torch.Tenso
 
 
 def sol_attn_fused(q, k, v, out, beta: float, flags: int, workspace: torch.Tensor, *,
-                   kept_per_row=None, mask_bits=None, tau=None, stream=None) -> None:
+                   kept_per_row=None, mask_bits=None, tau=None, item_clock=None, stream=None) -> None:
     _dev(q, k, v, out, workspace)
     B, H, N, d = _shape(q)
     flags |= _dtype_flag(q, k, v, out)
     _check(load_library().sol_attn_fused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                          B, H, N, d, float(beta), flags, workspace.data_ptr(),
-                                         workspace.numel(), _dbg(kept_per_row, mask_bits, tau),
+                                         workspace.numel(), _dbg(kept_per_row, mask_bits, tau, item_clock),
                                          _stream(stream)))
 
 
 def sol_attn_fwd_ex(q, k, v, out, beta: float, flags: int, stream=None,
                     workspace: Optional[torch.Tensor] = None, *, kept_per_row=None,
-                    mask_bits=None, tau=None) -> None:
+                    mask_bits=None, tau=None, item_clock=None) -> None:
     _dev(q, k, v, out)
     B, H, N, d = _shape(q)
     flags |= _dtype_flag(q, k, v, out)
@@ -197,7 +198,7 @@ def sol_attn_fwd_ex(q, k, v, out, beta: float, flags: int, stream=None,
     _check(load_library().sol_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                           B, H, N, d, float(beta), flags, _stream(stream),
                                           workspace.data_ptr(), workspace.numel(),
-                                          _dbg(kept_per_row, mask_bits, tau)))
+                                          _dbg(kept_per_row, mask_bits, tau, item_clock)))
 
 
 def sol_attn_fwd(q, k, v, out, beta: float, flags: int) -> None:

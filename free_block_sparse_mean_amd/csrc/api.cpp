@@ -130,6 +130,7 @@ sol_status fused_checked(const sol::Shape& s, const void* q, const void* k, cons
   a.kept_per_row = dbg ? dbg->kept_per_row : nullptr;
   a.mask_bits = dbg ? dbg->mask_bits : nullptr;
   a.tau = dbg ? dbg->tau : nullptr;
+  a.item_clock = dbg ? dbg->item_clock : nullptr;
   hipError_t e = sol::launch_fused(s, dtype_of(flags), a, st);
   if (e != hipSuccess) return device_fail(e, "fused kernel launch");
   return SOL_OK;

@@ -73,6 +73,7 @@ struct FusedParams {
   int32_t* kept_per_row;
   uint64_t* mask_bits;
   float* tau_out;
+  uint64_t* item_clock;
 };
 
 template <typename T, int D> struct Geom;
@@ -478,6 +479,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (bh >= p.BH || grp_id >= p.n_groups) return;   // uniform over the workgroup
   const int qi0 = grp_id * p.G;
   const int nG = min(p.G, n_b - qi0);
+  // optional work-item timing (debug): 100 MHz constant clock at start and end
+  const unsigned long long clk0 = p.item_clock ? __builtin_amdgcn_s_memrealtime() : 0ull;
 
   constexpr bool kBF = std::is_same<T, __bf16>::value;
   __shared__ __attribute__((aligned(16))) unsigned char sbufA[Gm::kBufBytes];
@@ -788,6 +791,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       epilogue<T, D>(st, p, bh, qi0 + g, g, row, lane, qa, misc);
     }
   }
+  if (p.item_clock) {
+    __syncthreads();   // every wave of the workgroup is done
+    if (t == 0) {
+      uint64_t* c = p.item_clock + 2 * ((size_t)bh * n_b + qi0);
+      c[0] = clk0;
+      c[1] = __builtin_amdgcn_s_memrealtime();
+    }
+  }
 }
 
 template <typename T, int D>
@@ -803,6 +814,7 @@ hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
   p.N = s.N;
   p.beta = a.beta; p.beta_mode = a.beta_mode;
   p.kept_per_row = a.kept_per_row; p.mask_bits = a.mask_bits; p.tau_out = a.tau;
+  p.item_clock = a.item_clock;
   const dim3 grid((unsigned)(8 * g.per_xcd * s.BH()));
   if (a.correction) {
     auto k = fused_kernel<T, D, true>;

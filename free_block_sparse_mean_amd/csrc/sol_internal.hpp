@@ -66,6 +66,7 @@ struct FusedArgs {
   int32_t* kept_per_row;
   uint64_t* mask_bits;
   float* tau;
+  uint64_t* item_clock;
 };
 
 // Each returns the first HIP error of its launches (hipSuccess otherwise).

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SOL_ATTN_ABI_VERSION 1
+#define SOL_ATTN_ABI_VERSION 2
 
 typedef enum sol_status {
   SOL_OK = 0,
@@ -71,11 +71,18 @@ typedef enum sol_status {
  * n_b = N / 64, W = ceil(n_b / 64).
  *   kept_per_row [B*H*n_b]      int32: |S_i| for each query block (row of blocks)
  *   mask_bits    [B*H*n_b*W]    uint64: bit (j % 64) of word j / 64 is set iff j in S_i
- *   tau          [B*H*n_b]      float: tau_i as used by the selection (-inf / +inf allowed) */
+ *   tau          [B*H*n_b]      float: tau_i as used by the selection (-inf / +inf allowed)
+ *   item_clock   [B*H*n_b][2]   uint64: for the workgroup whose first query block is i of
+ *                               head (b, h), entry (b*H + h)*n_b + i holds the device's
+ *                               100 MHz constant clock (s_memrealtime) when the workgroup
+ *                               started and when its last wave finished; entries of query
+ *                               blocks that start no workgroup are left untouched (a
+ *                               workgroup takes up to 4 consecutive query blocks) */
 typedef struct sol_debug {
   int32_t*  kept_per_row;
   uint64_t* mask_bits;
   float*    tau;
+  uint64_t* item_clock;
 } sol_debug;
 
 /* Byte offsets, inside a workspace, of the arrays the block-summary pre-pass

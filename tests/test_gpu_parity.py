@@ -162,3 +162,25 @@ def test_prepass_summaries(w, gpu_lib):
             np.testing.assert_allclose(views["vsum"][b, h], 64 * vbar, rtol=0, atol=64e-6 * np.abs(vbar).max())
             np.testing.assert_allclose(views["kmean"][b, h], m, rtol=0, atol=1e-6 * sc)
             np.testing.assert_allclose(views["kcov"][b, h], C, rtol=0, atol=1e-5 * np.abs(C).max())
+
+
+def test_item_clock_export(gpu_lib):
+    """The optional work-item clock: one (start, end) pair per workgroup, at the entry of its
+    first query block; workgroups take G consecutive blocks; other entries untouched."""
+    w = SMALL[1]
+    q, k, v = (t.cuda() for t in wl.make_qkv(w))
+    nb = w.n_blocks
+    ws = gpu_lib.new_workspace(w.B, w.H, w.N, w.d)
+    out = torch.empty_like(q)
+    clk = torch.zeros((w.B * w.H * nb, 2), dtype=torch.int64, device=q.device)
+    gpu_lib.sol_block_summaries(k, v, ws)
+    gpu_lib.sol_attn_fused(q, k, v, out, 1.0, gpu_lib.SOL_CORRECTION, ws, item_clock=clk)
+    torch.cuda.synchronize()
+    c = clk.cpu().view(w.B * w.H, nb, 2)
+    set_ = c[..., 0] != 0
+    starts = torch.nonzero(set_[0]).flatten().tolist()
+    G = starts[1] - starts[0] if len(starts) > 1 else nb
+    assert 1 <= G <= 4 and starts == list(range(0, nb, G))
+    assert bool((set_ == set_[0]).all())                      # the same pattern in every head
+    assert bool((c[..., 1][set_] >= c[..., 0][set_]).all())
+    assert bool((c[..., 1][~set_] == 0).all())

@@ -152,6 +152,36 @@ def load_balance(sb, qd, kd, vd, out, ws, beta, flags, w) -> dict:
             "p99_over_mean": float(np.percentile(busy, 99) / m), "launch_span_us": float(span)}
 
 
+def routing_overhead(sb, qd, kd, vd, out, ws, beta, w, steps) -> dict:
+    """Kernel-time ablation at one beta on the same selection: the fused pass with and
+    without the correction against plain block-sparse attention on the routing's own
+    mask (sol_attn_masked: no routing, no correction). Pre-pass done beforehand, untimed."""
+    import torch
+    nb = w.n_blocks
+    words = torch.zeros((w.B, w.H, nb, (nb + 63) // 64), dtype=torch.int64, device=qd.device)
+    sb.sol_block_summaries(kd, vd, ws)
+    sb.sol_attn_fused(qd, kd, vd, out, beta, 0, ws, mask_bits=words)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        fn()
+        st = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(st)
+            fn()
+            b.record(st)
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in ev)
+
+    masked = timed(lambda: sb.sol_attn_masked(qd, kd, vd, out, words, 0, ws))
+    nocorr = timed(lambda: sb.sol_attn_fused(qd, kd, vd, out, beta, 0, ws))
+    withcorr = timed(lambda: sb.sol_attn_fused(qd, kd, vd, out, beta, sb.SOL_CORRECTION, ws))
+    return {"beta": beta, "reps": steps, "given_mask_ms": masked, "fused_no_correction_ms": nocorr,
+            "fused_ms": withcorr, "routing_overhead": nocorr / masked - 1.0,
+            "routing_and_correction_overhead": withcorr / masked - 1.0}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -244,6 +274,7 @@ def main() -> int:
     head = measure(args.beta, corr, args.steps, args.warmup)
     rows = row_stats(kept)
     balance = load_balance(sb, qd, kd, vd, out, ws, args.beta, corr, w)
+    ablation = routing_overhead(sb, qd, kd, vd, out, ws, args.beta, w, max(3, args.steps // 2))
     # the two-call step equals one sol_attn_fwd_ex call (bit for bit)
     ref = out.clone()
     sb.sol_attn_fwd_ex(qd, kd, vd, out, args.beta, corr, workspace=ws)
@@ -295,6 +326,7 @@ def main() -> int:
         "per_beta": per_beta,
         "kept_per_row": rows,
         "load_balance": balance,
+        "routing_ablation": ablation,
         "prepass": {"ms": head["prepass_ms"], "hbm_gbs": head["prepass_hbm_gbs"],
                     "frac": head["prepass_hbm_gbs"] / PEAK_HBM_GBS},
         "checks": {"two_call_step_equals_fwd_ex": same_as_fwd_ex},

@@ -76,6 +76,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sol_attn_fused.argtypes = [vp, vp, vp, vp, i, i, i, i, f, u, vp, sz,
                                    ctypes.POINTER(sol_debug), vp]
     lib.sol_attn_fused.restype = i
+    lib.sol_attn_masked.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, u, vp, sz, vp, vp]
+    lib.sol_attn_masked.restype = i
     lib.sol_attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, f, u, vp, vp, sz,
                                     ctypes.POINTER(sol_debug)]
     lib.sol_attn_fwd_ex.restype = i
@@ -185,6 +187,21 @@ def sol_attn_fused(q, k, v, out, beta: float, flags: int, workspace: torch.Tenso
                                          B, H, N, d, float(beta), flags, workspace.data_ptr(),
                                          workspace.numel(), _dbg(kept_per_row, mask_bits, tau, item_clock),
                                          _stream(stream)))
+
+
+def sol_attn_masked(q, k, v, out, mask_bits: torch.Tensor, flags: int, workspace: torch.Tensor, *,
+                    kept_per_row=None, stream=None) -> None:
+    """Block-sparse attention on a given selection (mask_bits: int64 [B, H, n_b, W] words)."""
+    _dev(q, k, v, out, mask_bits, workspace)
+    B, H, N, d = _shape(q)
+    if mask_bits.dtype != torch.int64 or mask_bits.numel() != B * H * (N // BLOCK) * ((N // BLOCK + 63) // 64):
+        raise ValueError("mask_bits must be int64 [B, H, n_b, ceil(n_b/64)]")
+    flags |= _dtype_flag(q, k, v, out)
+    _check(load_library().sol_attn_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                          B, H, N, d, mask_bits.data_ptr(), flags, workspace.data_ptr(),
+                                          workspace.numel(),
+                                          None if kept_per_row is None else kept_per_row.data_ptr(),
+                                          _stream(stream)))
 
 
 def sol_attn_fwd_ex(q, k, v, out, beta: float, flags: int, stream=None,

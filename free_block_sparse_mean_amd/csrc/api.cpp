@@ -131,6 +131,7 @@ sol_status fused_checked(const sol::Shape& s, const void* q, const void* k, cons
   a.mask_bits = dbg ? dbg->mask_bits : nullptr;
   a.tau = dbg ? dbg->tau : nullptr;
   a.item_clock = dbg ? dbg->item_clock : nullptr;
+  a.mask_in = nullptr;
   hipError_t e = sol::launch_fused(s, dtype_of(flags), a, st);
   if (e != hipSuccess) return device_fail(e, "fused kernel launch");
   return SOL_OK;
@@ -214,6 +215,38 @@ sol_status sol_attn_fused(const void* q, const void* k, const void* v, void* out
                 ws_bytes, workspace ? "" : ", NULL");
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str)) != SOL_OK) return st;
+  return finish(flags, str);
+}
+
+sol_status sol_attn_masked(const void* q, const void* k, const void* v, void* out, int B, int H,
+                           int N, int d, const uint64_t* mask_bits, unsigned flags,
+                           const void* workspace, size_t ws_bytes, int32_t* kept_per_row,
+                           void* hip_stream) {
+  sol::Shape s;
+  sol_status st = check_shape(B, H, N, d, &s);
+  if (st != SOL_OK) return st;
+  if (!q || !k || !v || !out || !mask_bits)
+    return fail(SOL_ERR_INVALID_ARG, "q, k, v, out and mask_bits must be non-null");
+  if ((st = check_flags(flags)) != SOL_OK) return st;
+  if (flags & (SOL_CORRECTION | SOL_DENSE))
+    return fail(SOL_ERR_INVALID_ARG, "the given-mask mode takes neither SOL_CORRECTION nor SOL_DENSE");
+  if (!workspace || ws_bytes < sol::make_layout(s).total)
+    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
+                ws_bytes, workspace ? "" : ", NULL");
+  hipStream_t str = static_cast<hipStream_t>(hip_stream);
+  sol::FusedArgs a;
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.ws = sol::bind_workspace(s, const_cast<void*>(workspace));
+  a.beta = 0.f;
+  a.beta_mode = sol::kBetaFinite;
+  a.correction = false;
+  a.kept_per_row = kept_per_row;
+  a.mask_bits = nullptr;
+  a.tau = nullptr;
+  a.item_clock = nullptr;
+  a.mask_in = mask_bits;
+  hipError_t e = sol::launch_fused(s, dtype_of(flags), a, str);
+  if (e != hipSuccess) return device_fail(e, "given-mask kernel launch");
   return finish(flags, str);
 }
 

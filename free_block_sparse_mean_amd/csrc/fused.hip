@@ -74,6 +74,7 @@ struct FusedParams {
   uint64_t* mask_bits;
   float* tau_out;
   uint64_t* item_clock;
+  const uint64_t* mask_in;   // caller-given selection (kModeGiven), [BH][n_b][n_words]
 };
 
 template <typename T, int D> struct Geom;
@@ -457,8 +458,13 @@ __device__ __forceinline__ void epilogue(ExactState<T, D>& st, const FusedParams
   }
 }
 
-template <typename T, int D, bool CORR>
+// Kernel modes: routing without / with the correction, or a caller-given
+// block mask (plain block-sparse attention: no routing, no correction).
+constexpr int kModeRoute = 0, kModeCorr = 1, kModeGiven = 2;
+
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel(FusedParams p) {
+  constexpr bool CORR = MODE == kModeCorr;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   using Gm = Geom<T, D>;
   using L = Lds<T, D>;
@@ -505,6 +511,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const T* Kh = static_cast<const T*>(p.k) + (size_t)bh * p.N * D;
   const T* Vh = static_cast<const T*>(p.v) + (size_t)bh * p.N * D;
 
+  if constexpr (MODE == kModeGiven) {
+    // ---- caller-given selection: the G blocks' mask words into LDS ----------
+    for (int e = t; e < nG * n_words; e += 256) {
+      const int g = e / n_words, wi = e % n_words;
+      uint64_t word = p.mask_in[(bh * n_b + qi0 + g) * (long long)n_words + wi];
+      if (wi == n_words - 1 && (n_b & 63)) word &= (1ull << (n_b & 63)) - 1;   // bits past n_b ignored
+      masks[g * n_words + wi] = word;
+    }
+    if (t < kGMax) {
+      misc[kC2 + t] = -INFINITY;   // no correction term
+      misc[kL + t] = 0.f;
+    }
+    __syncthreads();
+    if (p.kept_per_row && t < nG) {
+      int c = 0;
+      for (int wi = 0; wi < n_words; ++wi) c += __popcll(masks[t * n_words + wi]);
+      p.kept_per_row[bh * n_b + qi0 + t] = c;
+    }
+  } else {
   // ---- 1. q_bar of the G query blocks ---------------------------------------
   {
     using V16 = Vec16<T>;
@@ -703,6 +728,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   }
+  }   // routing
   __syncthreads();   // masks, A, L, c2 visible; the proxy rows are dead
 
   // ---- 5. inner loop: exact attention on the kept tiles ---------------------
@@ -815,18 +841,16 @@ hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
   p.beta = a.beta; p.beta_mode = a.beta_mode;
   p.kept_per_row = a.kept_per_row; p.mask_bits = a.mask_bits; p.tau_out = a.tau;
   p.item_clock = a.item_clock;
+  p.mask_in = a.mask_in;
   const dim3 grid((unsigned)(8 * g.per_xcd * s.BH()));
-  if (a.correction) {
-    auto k = fused_kernel<T, D, true>;
-    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, dim3(256), g.lds_bytes, st, p);
-  } else {
-    auto k = fused_kernel<T, D, false>;
-    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, dim3(256), g.lds_bytes, st, p);
-  }
+  const void* fn = a.mask_in      ? (const void*)fused_kernel<T, D, kModeGiven>
+                   : a.correction ? (const void*)fused_kernel<T, D, kModeCorr>
+                                  : (const void*)fused_kernel<T, D, kModeRoute>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
+  if (e != hipSuccess) return e;
+  void* args[] = {&p};
+  e = hipLaunchKernel(fn, grid, dim3(256), args, g.lds_bytes, st);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

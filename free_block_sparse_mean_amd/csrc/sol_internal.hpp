@@ -67,6 +67,7 @@ struct FusedArgs {
   uint64_t* mask_bits;
   float* tau;
   uint64_t* item_clock;
+  const uint64_t* mask_in;   // non-null: caller-given selection, no routing and no correction
 };
 
 // Each returns the first HIP error of its launches (hipSuccess otherwise).

@@ -143,6 +143,25 @@ sol_status sol_attn_fused(const void* q, const void* k, const void* v, void* out
                           const void* workspace, size_t ws_bytes, const sol_debug* dbg,
                           void* hip_stream);
 
+/* Block-sparse attention on a caller-given selection: no routing and no
+ * correction, the same exact-attention pass as sol_attn_fused on the same
+ * blocks. It is the plain block-sparse kernel the fused pass is measured
+ * against (page "Sol-Attn: l'attenzione sparsa che sceglie al volo"
+ * (paithon.it), section "I numeri": the fused kernel against a plain
+ * block-sparse kernel on the same blocks). Needs the pre-pass workspace of
+ * the same K, V (sol_block_summaries).
+ *   mask_bits    [B*H*n_b*W] uint64, device, same layout as sol_debug.mask_bits:
+ *                bit (j % 64) of word j / 64 of query block i keeps key block j;
+ *                bits past n_b are ignored. A query block with no bit set gets
+ *                zero output rows.
+ *   kept_per_row [B*H*n_b] int32, device, optional (NULL): popcount of each row.
+ * flags: SOL_F32 and SOL_SYNC only; SOL_CORRECTION or SOL_DENSE give
+ * SOL_ERR_INVALID_ARG. Asynchronous on hip_stream like sol_attn_fused. */
+sol_status sol_attn_masked(const void* q, const void* k, const void* v, void* out,
+                           int B, int H, int N, int d, const uint64_t* mask_bits,
+                           unsigned flags, const void* workspace, size_t ws_bytes,
+                           int32_t* kept_per_row, void* hip_stream);
+
 /* Whole forward on a caller stream with a caller workspace:
  * sol_block_summaries followed by sol_attn_fused. Reentrant. */
 sol_status sol_attn_fwd_ex(const void* q, const void* k, const void* v, void* out,

@@ -89,3 +89,15 @@ def test_layout_offsets(lib):
     assert offs == sorted(offs) and offs[0] == 0 and lay.total_bytes > lay.scratch
     assert all(o % 256 == 0 for o in offs)
     assert lay.kbar - lay.kbar_t >= 6 * 128 * 100 * 4
+
+
+def test_masked_validation(lib):
+    """The given-mask entry point checks its arguments before any device call."""
+    p = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    assert lib.sol_attn_masked(p, p, p, p, 1, 1, 4096, 64, None, 0, p, 1 << 30, None, None) == 1
+    assert "mask_bits" in lib.sol_last_error().decode()
+    assert lib.sol_attn_masked(p, p, p, p, 1, 1, 4096, 64, p, 0x2, p, 1 << 30, None, None) == 1
+    assert "SOL_CORRECTION" in lib.sol_last_error().decode()
+    assert lib.sol_attn_masked(p, p, p, p, 1, 1, 4096, 64, p, 0x4, p, 1 << 30, None, None) == 1
+    assert lib.sol_attn_masked(p, p, p, p, 1, 1, 4096, 64, p, 0, p, 10, None, None) == 5
+    assert lib.sol_attn_masked(p, p, p, p, 1, 1, 4096, 96, p, 0, p, 1 << 30, None, None) == 2

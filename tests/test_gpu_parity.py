@@ -184,3 +184,67 @@ def test_item_clock_export(gpu_lib):
     assert bool((set_ == set_[0]).all())                      # the same pattern in every head
     assert bool((c[..., 1][set_] >= c[..., 0][set_]).all())
     assert bool((c[..., 1][~set_] == 0).all())
+
+
+def _encode_mask(mask: np.ndarray, pad_bits: bool) -> torch.Tensor:
+    """bool [..., n_b] -> int64 words [..., W]; bits past n_b set when pad_bits (to be ignored)."""
+    nb = mask.shape[-1]
+    W = (nb + 63) // 64
+    full = np.zeros(mask.shape[:-1] + (W * 64,), dtype=bool)
+    full[..., :nb] = mask
+    if pad_bits:
+        full[..., nb:] = True
+    words = np.packbits(full.reshape(-1, W, 64), axis=-1, bitorder="little").view(np.int64)
+    return torch.from_numpy(words.reshape(mask.shape[:-1] + (W,)).copy())
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[1], SMALL[2], SMALL[6]], ids=lambda w: w.name)
+def test_masked_parity(w, gpu_lib):
+    """Given-mask block-sparse mode against the oracle run with the same mask (no correction);
+    rows with no kept block give zeros; bits past n_b are ignored."""
+    print(f"case masked {w.name}", flush=True)
+    q, k, v = wl.make_qkv(w)
+    nb = w.n_blocks
+    rng = np.random.default_rng(7)
+    mask = rng.random((w.B, w.H, nb, nb)) < 0.2
+    mask[:, :, 1, :] = False                                   # an empty row
+    mask[:, :, 2, :] = True                                    # a dense row
+    words = _encode_mask(mask, pad_bits=True).cuda()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    ws = gpu_lib.new_workspace(w.B, w.H, w.N, w.d)
+    gpu_lib.sol_block_summaries(kd, vd, ws)
+    out = torch.empty_like(qd)
+    kept = torch.full((w.B, w.H, nb), -1, dtype=torch.int32, device=qd.device)
+    gpu_lib.sol_attn_masked(qd, kd, vd, out, words, 0, ws, kept_per_row=kept)
+    torch.cuda.synchronize()
+    assert torch.equal(kept.cpu(), torch.from_numpy(mask.sum(-1).astype(np.int32)))
+    got = out.float().cpu().numpy()
+    rel_tol, abs_tol = (pu.BF16_REL_L2, pu.BF16_MAX_ABS) if w.dtype == BF else (pu.F32_REL_L2, pu.F32_MAX_ABS)
+    from oracle import sol_oracle as orc
+    for b in range(w.B):
+        for h in range(w.H):
+            ref = orc.sol_attention_head(q[b, h].float().numpy(), k[b, h].float().numpy(),
+                                         v[b, h].float().numpy(), 0.0, False,
+                                         mask_override=mask[b, h])["out"]
+            g = got[b, h]
+            assert np.all(g[64:128] == 0.0)
+            r, a = pu.rel_l2(g, ref), float(np.abs(g - ref).max())
+            assert r <= rel_tol and a <= abs_tol, f"{w.name} b{b} h{h}: rel-L2 {r:.3e} max-abs {a:.3e}"
+
+
+def test_masked_equals_fused_without_correction(gpu_lib):
+    """On the routing's own selection the given-mask mode is the fused pass without the
+    correction, bit for bit."""
+    w = SMALL[1]
+    q, k, v = (t.cuda() for t in wl.make_qkv(w))
+    nb = w.n_blocks
+    W = (nb + 63) // 64
+    ws = gpu_lib.new_workspace(w.B, w.H, w.N, w.d)
+    gpu_lib.sol_block_summaries(k, v, ws)
+    a = torch.empty_like(q)
+    words = torch.zeros((w.B, w.H, nb, W), dtype=torch.int64, device=q.device)
+    gpu_lib.sol_attn_fused(q, k, v, a, 1.0, 0, ws, mask_bits=words)
+    b = torch.empty_like(q)
+    gpu_lib.sol_attn_masked(q, k, v, b, words, 0, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

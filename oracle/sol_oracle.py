@@ -39,6 +39,10 @@ Readings where the pages are silent (listed with reasons in the design notes):
   * beta = -inf keeps every block (tau = -inf, no -inf*0); beta = +inf keeps none;
   * a row with no kept block and the correction off outputs zeros;
   * the correction logit is the block-level s_hat_ij (not a per-row q_r.k_bar_j).
+
+The two routing baselines the pages compare the threshold with, top-k and
+top-p, are stated too (select_topk, select_topp); they select from the same
+proxy row.
 """
 from __future__ import annotations
 
@@ -127,6 +131,43 @@ def thresholds(mu: np.ndarray, sigma: np.ndarray, beta: float) -> np.ndarray:
 def select_blocks(s_hat: np.ndarray, tau: np.ndarray) -> np.ndarray:
     """S_i = {j : s_hat_ij > tau_i}, strict ([IT] "Una soglia per ogni riga", equation)."""
     return s_hat > tau[:, None]
+
+
+def select_topk(s_hat: np.ndarray, k: int) -> np.ndarray:
+    """Top-k routing, the baseline the pages set against the threshold: each row
+    keeps its k highest proxy scores ([IT] "Perché l'attenzione pesa tanto nei
+    video"). Equal scores are taken in ascending j (reading: the pages give no
+    tie rule). k is clamped to [0, n_b]."""
+    n_rows, nb = s_hat.shape
+    k = max(0, min(int(k), nb))
+    keep = np.zeros((n_rows, nb), dtype=bool)
+    for i in range(n_rows):
+        order = sorted(range(nb), key=lambda j: (-float(s_hat[i, j]), j))
+        keep[i, order[:k]] = True
+    return keep
+
+
+def select_topp(s_hat: np.ndarray, p: float) -> np.ndarray:
+    """Top-p routing: each row keeps blocks, best proxy score first, until their
+    cumulative probability reaches p ([IT] "Perché l'attenzione pesa tanto nei
+    video"). Readings: the probability of block j is the softmax of the row's
+    proxy scores (the scores as logits); the block whose addition reaches p is
+    kept; equal scores are taken in ascending j; when rounding keeps the total
+    below p every block is kept. Accumulated in float64."""
+    n_rows, nb = s_hat.shape
+    keep = np.zeros((n_rows, nb), dtype=bool)
+    for i in range(n_rows):
+        row = s_hat[i].astype(np.float64)
+        w = np.exp(row - row.max())
+        prob = w / w.sum()
+        order = sorted(range(nb), key=lambda j: (-float(s_hat[i, j]), j))
+        acc = 0.0
+        for j in order:
+            keep[i, j] = True
+            acc += prob[j]
+            if acc >= p:
+                break
+    return keep
 
 
 def _attend_query_block(qi: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,

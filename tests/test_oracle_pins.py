@@ -346,3 +346,76 @@ def test_rejects_bad_inputs():
         orc.block_means(np.zeros((65, 4)))
     with pytest.raises(ValueError):
         orc.thresholds(np.zeros(2), np.ones(2), float("nan"))
+
+
+# ---- routing baselines: top-k and top-p ------------------------------------
+
+def _subsets(n):
+    import itertools
+    for m in range(n + 1):
+        for c in itertools.combinations(range(n), m):
+            yield c
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_topk_is_the_best_k_subset(seed):
+    """Brute force over every subset of a tiny row: the kept set has exactly k blocks and
+    the largest score sum of all k-subsets; with integer scores ties resolve to lower j."""
+    rng = _rng(40 + seed)
+    s = rng.integers(-3, 4, size=(5, 7)).astype(np.float64)
+    for k in range(0, 9):
+        keep = orc.select_topk(s, k)
+        kk = min(k, 7)
+        assert (keep.sum(1) == kk).all()
+        for i in range(s.shape[0]):
+            best = max(sum(s[i, list(c)]) for c in _subsets(7) if len(c) == kk)
+            assert sum(s[i, keep[i]]) == best
+            # among equal scores at the boundary, the lower index is kept
+            kept_idx = np.flatnonzero(keep[i])
+            dropped = np.flatnonzero(~keep[i])
+            for a in kept_idx:
+                for b in dropped:
+                    assert s[i, a] > s[i, b] or (s[i, a] == s[i, b] and a < b)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_topp_is_the_smallest_set_reaching_p(seed):
+    """Brute force over every subset of a tiny row: the kept set reaches probability mass p,
+    no smaller set does, and it holds the highest scores."""
+    rng = _rng(50 + seed)
+    s = rng.standard_normal((4, 7))
+    prob = np.exp(s - s.max(1, keepdims=True))
+    prob /= prob.sum(1, keepdims=True)
+    for p in (0.05, 0.3, 0.5, 0.77, 0.95, 0.999):
+        keep = orc.select_topp(s, p)
+        for i in range(s.shape[0]):
+            m = keep[i].sum()
+            assert prob[i, keep[i]].sum() >= p - 1e-12
+            smallest = min(len(c) for c in _subsets(7) if prob[i, list(c)].sum() >= p - 1e-12)
+            assert m == smallest
+            assert s[i, keep[i]].min() >= s[i, ~keep[i]].max(initial=-np.inf)
+
+
+def test_topp_flat_row_keeps_ceil_p_n():
+    """A flat proxy row spreads the probability evenly: top-p keeps ceil(p * n_b) blocks,
+    the upper end of the range the pages give; a dominant block alone reaches p."""
+    s = np.zeros((1, 8))
+    for p, want in ((0.125, 1), (0.5, 4), (0.625, 5), (1.0, 8)):
+        assert orc.select_topp(s, p).sum() == want
+    s = np.array([[20.0, 0.0, 0.0, 0.0]])
+    assert orc.select_topp(s, 0.9).tolist() == [[True, False, False, False]]
+
+
+def test_topk_topp_monotone():
+    rng = _rng(60)
+    s = rng.standard_normal((6, 40))
+    prev = np.zeros_like(s, dtype=bool)
+    for k in range(0, 41, 5):
+        cur = orc.select_topk(s, k)
+        assert (cur >= prev).all()
+        prev = cur
+    prev = np.zeros_like(s, dtype=bool)
+    for p in (0.1, 0.3, 0.6, 0.9):
+        cur = orc.select_topp(s, p)
+        assert (cur >= prev).all()
+        prev = cur

@@ -182,6 +182,59 @@ def routing_overhead(sb, qd, kd, vd, out, ws, beta, w, steps) -> dict:
             "routing_and_correction_overhead": withcorr / masked - 1.0}
 
 
+def routing_study(sb, qd, kd, vd, out, ws, w, steps) -> dict:
+    """Routing cost and per-row budget at about 15% mean density (the pages' ablation
+    point): the fused pass's in-pass threshold routing (beta = +inf, no correction: the
+    proxy scan and test with no exact tile) against the baselines that materialize the
+    proxy map (sol_route: threshold from the map, top-k, top-p). beta, k and p are
+    chosen for 15% mean density on this workload (calibrated offline with the oracle's
+    selection rules on three heads)."""
+    import numpy as np
+    import torch
+    nb = w.n_blocks
+    W = (nb + 63) // 64
+    dev = qd.device
+    pm = torch.empty((w.B, w.H, nb, nb), dtype=torch.float32, device=dev)
+    words = torch.zeros((w.B, w.H, nb, W), dtype=torch.int64, device=dev)
+    kept = torch.zeros((w.B, w.H, nb), dtype=torch.int32, device=dev)
+    sb.sol_block_summaries(kd, vd, ws)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        fn()
+        st = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(st)
+            fn()
+            b.record(st)
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in ev)
+
+    def spread():
+        x = kept.flatten().cpu().numpy().astype(np.float64) / nb
+        m = float(x.mean())
+        return {"mean_density": m, "row_cv": float(x.std() / m) if m else None,
+                "row_min_over_mean": float(x.min() / m) if m else None,
+                "row_max_over_mean": float(x.max() / m) if m else None,
+                "row_p99_over_mean": float(np.percentile(x, 99) / m) if m else None}
+
+    res = {"proxy_map_bytes": 4 * w.B * w.H * nb * nb, "reps": steps}
+    fused_route = timed(lambda: sb.sol_attn_fused(qd, kd, vd, out, math.inf, 0, ws))
+    res["fused_threshold_routing_ms"] = fused_route
+    sb.sol_attn_fused(qd, kd, vd, out, 1.1, 0, ws, kept_per_row=kept)
+    torch.cuda.synchronize()
+    res["fused_threshold"] = dict(beta=1.1, **spread())
+    k = int(round(0.15 * nb))
+    for name, kw in (("threshold_map", dict(beta=1.1)), ("top_k", dict(top_k=k)), ("top_p", dict(top_p=0.66))):
+        mode = {"threshold_map": sb.SOL_ROUTE_THRESHOLD, "top_k": sb.SOL_ROUTE_TOPK, "top_p": sb.SOL_ROUTE_TOPP}[name]
+        ms = timed(lambda: sb.sol_route(qd, mode, ws, pm, words, **kw))
+        sb.sol_route(qd, mode, ws, pm, words, kept_per_row=kept, **kw)
+        torch.cuda.synchronize()
+        res[name] = dict(routing_ms=ms, **kw, **spread())
+    return res
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -203,6 +256,7 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true", help="skip timing the dense path")
     ap.add_argument("--no-correction", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-routing-study", action="store_true")
     ap.add_argument("--cpu-blocks-per-head", type=int, default=128)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (for counter scaling)")
@@ -275,6 +329,7 @@ def main() -> int:
     rows = row_stats(kept)
     balance = load_balance(sb, qd, kd, vd, out, ws, args.beta, corr, w)
     ablation = routing_overhead(sb, qd, kd, vd, out, ws, args.beta, w, max(3, args.steps // 2))
+    study = None if args.no_routing_study else routing_study(sb, qd, kd, vd, out, ws, w, 5)
     # the two-call step equals one sol_attn_fwd_ex call (bit for bit)
     ref = out.clone()
     sb.sol_attn_fwd_ex(qd, kd, vd, out, args.beta, corr, workspace=ws)
@@ -327,6 +382,7 @@ def main() -> int:
         "kept_per_row": rows,
         "load_balance": balance,
         "routing_ablation": ablation,
+        "routing_study": study,
         "prepass": {"ms": head["prepass_ms"], "hbm_gbs": head["prepass_hbm_gbs"],
                     "frac": head["prepass_hbm_gbs"] / PEAK_HBM_GBS},
         "checks": {"two_call_step_equals_fwd_ex": same_as_fwd_ex},

@@ -30,6 +30,10 @@ SOL_CORRECTION = 0x2
 SOL_DENSE = 0x4
 SOL_SYNC = 0x8
 
+SOL_ROUTE_THRESHOLD = 0
+SOL_ROUTE_TOPK = 1
+SOL_ROUTE_TOPP = 2
+
 BLOCK = 64
 
 
@@ -48,7 +52,7 @@ class sol_debug(ctypes.Structure):
 
 class sol_workspace_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("total_bytes", "kbar_t", "kbar", "vsum", "kmean", "kcov", "vt", "scratch")]
+                ("total_bytes", "kbar_t", "kbar", "vsum", "kmean", "kcov", "vt", "qbar", "scratch")]
 
 
 _lib = None
@@ -76,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sol_attn_fused.argtypes = [vp, vp, vp, vp, i, i, i, i, f, u, vp, sz,
                                    ctypes.POINTER(sol_debug), vp]
     lib.sol_attn_fused.restype = i
+    lib.sol_route.argtypes = [vp, i, i, i, i, u, i, f, i, f, vp, sz, vp, vp, vp, vp, vp]
+    lib.sol_route.restype = i
     lib.sol_attn_masked.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, u, vp, sz, vp, vp]
     lib.sol_attn_masked.restype = i
     lib.sol_attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, f, u, vp, vp, sz,
@@ -165,6 +171,7 @@ def workspace_views(ws: torch.Tensor, B: int, H: int, N: int, d: int) -> Dict[st
         "kmean": f32(lay.kmean, (B, H, d)),
         "kcov": f32(lay.kcov, (B, H, d, d)),
         "vt": ws[lay.vt:lay.vt + 2 * B * H * N * d].view(torch.bfloat16).view(B, H, nb, d, BLOCK),
+        "qbar": f32(lay.qbar, (B, H, nb, d)),
     }
 
 
@@ -187,6 +194,26 @@ def sol_attn_fused(q, k, v, out, beta: float, flags: int, workspace: torch.Tenso
                                          B, H, N, d, float(beta), flags, workspace.data_ptr(),
                                          workspace.numel(), _dbg(kept_per_row, mask_bits, tau, item_clock),
                                          _stream(stream)))
+
+
+def sol_route(q, mode: int, workspace: torch.Tensor, proxy_map: torch.Tensor, mask_bits: torch.Tensor, *,
+              beta: float = 0.0, top_k: int = 0, top_p: float = 0.0, kept_per_row=None, topk_idx=None,
+              flags: int = 0, stream=None) -> None:
+    """Routing baseline with a materialized proxy map (float32 [B, H, n_b, n_b]); mask words
+    int64 [B, H, n_b, W] written; the workspace must hold the pre-pass of the same K."""
+    _dev(q, workspace, proxy_map, mask_bits)
+    B, H, N, d = _shape(q)
+    nb = N // BLOCK
+    if proxy_map.dtype != torch.float32 or proxy_map.numel() != B * H * nb * nb:
+        raise ValueError("proxy_map must be float32 [B, H, n_b, n_b]")
+    if mask_bits.dtype != torch.int64 or mask_bits.numel() != B * H * nb * ((nb + 63) // 64):
+        raise ValueError("mask_bits must be int64 [B, H, n_b, ceil(n_b/64)]")
+    flags |= _dtype_flag(q)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _check(load_library().sol_route(q.data_ptr(), B, H, N, d, flags, int(mode), float(beta), int(top_k),
+                                    float(top_p), workspace.data_ptr(), workspace.numel(),
+                                    proxy_map.data_ptr(), mask_bits.data_ptr(), ptr(kept_per_row),
+                                    ptr(topk_idx), _stream(stream)))
 
 
 def sol_attn_masked(q, k, v, out, mask_bits: torch.Tensor, flags: int, workspace: torch.Tensor, *,

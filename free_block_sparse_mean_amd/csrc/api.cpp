@@ -26,6 +26,7 @@ Layout make_layout(const Shape& s) {
   L.kmean = off;    off += up256(bh * d * 4);
   L.kcov = off;     off += up256(bh * d * d * 4);
   L.vt = off;       off += up256(bh * nb * d * 64 * 2);
+  L.qbar = off;     off += up256(bh * nb * d * 4);
   L.s1_part = off;  off += up256(bh * (size_t)s.cov_parts * d * 8);
   L.s2_part = off;  off += up256(bh * (size_t)s.cov_parts * d * d * 8);
   L.total = off;
@@ -42,6 +43,7 @@ Workspace bind_workspace(const Shape& s, void* base) {
   w.kmean = reinterpret_cast<float*>(b + L.kmean);
   w.kcov = reinterpret_cast<float*>(b + L.kcov);
   w.vt = reinterpret_cast<__bf16*>(b + L.vt);
+  w.qbar = reinterpret_cast<float*>(b + L.qbar);
   w.s1_part = reinterpret_cast<double*>(b + L.s1_part);
   w.s2_part = reinterpret_cast<double*>(b + L.s2_part);
   return w;
@@ -184,6 +186,7 @@ sol_status sol_attn_workspace_layout(int B, int H, int N, int d, sol_workspace_l
   layout->kmean = L.kmean;
   layout->kcov = L.kcov;
   layout->vt = L.vt;
+  layout->qbar = L.qbar;
   layout->scratch = L.s1_part;
   return ok();
 }
@@ -247,6 +250,44 @@ sol_status sol_attn_masked(const void* q, const void* k, const void* v, void* ou
   a.mask_in = mask_bits;
   hipError_t e = sol::launch_fused(s, dtype_of(flags), a, str);
   if (e != hipSuccess) return device_fail(e, "given-mask kernel launch");
+  return finish(flags, str);
+}
+
+sol_status sol_route(const void* q, int B, int H, int N, int d, unsigned flags, int mode,
+                     float beta, int topk, float topp, const void* workspace, size_t ws_bytes,
+                     float* proxy_map, uint64_t* mask_bits, int32_t* kept_per_row,
+                     int32_t* topk_idx, void* hip_stream) {
+  sol::Shape s;
+  sol_status st = check_shape(B, H, N, d, &s);
+  if (st != SOL_OK) return st;
+  if (!q || !proxy_map || !mask_bits)
+    return fail(SOL_ERR_INVALID_ARG, "q, proxy_map and mask_bits must be non-null");
+  if ((st = check_flags(flags)) != SOL_OK) return st;
+  if (flags & (SOL_CORRECTION | SOL_DENSE))
+    return fail(SOL_ERR_INVALID_ARG, "routing takes neither SOL_CORRECTION nor SOL_DENSE");
+  if (mode != SOL_ROUTE_THRESHOLD && mode != SOL_ROUTE_TOPK && mode != SOL_ROUTE_TOPP)
+    return fail(SOL_ERR_INVALID_ARG, "unknown routing mode %d", mode);
+  if (mode == SOL_ROUTE_THRESHOLD && isnan(beta)) return fail(SOL_ERR_INVALID_ARG, "beta is NaN");
+  if (mode == SOL_ROUTE_TOPP && !(topp == topp)) return fail(SOL_ERR_INVALID_ARG, "top_p is NaN");
+  if (mode == SOL_ROUTE_TOPK && topk < 0) return fail(SOL_ERR_INVALID_ARG, "top_k is negative");
+  if (!workspace || ws_bytes < sol::make_layout(s).total)
+    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
+                ws_bytes, workspace ? "" : ", NULL");
+  hipStream_t str = static_cast<hipStream_t>(hip_stream);
+  sol::RouteArgs a;
+  a.q = q;
+  a.ws = sol::bind_workspace(s, const_cast<void*>(workspace));
+  a.mode = mode;
+  a.beta = beta;
+  a.beta_mode = beta == -INFINITY ? sol::kBetaMinusInf : beta == INFINITY ? sol::kBetaPlusInf : sol::kBetaFinite;
+  a.topk = topk;
+  a.topp = topp;
+  a.proxy_map = proxy_map;
+  a.mask = mask_bits;
+  a.kept = kept_per_row;
+  a.idx = mode == SOL_ROUTE_TOPK ? topk_idx : nullptr;
+  hipError_t e = sol::launch_route(s, dtype_of(flags), a, str);
+  if (e != hipSuccess) return device_fail(e, "routing launch");
   return finish(flags, str);
 }
 

@@ -33,12 +33,13 @@ struct Workspace {
   float* kmean;     // [BH][d]
   float* kcov;      // [BH][d][d]
   __bf16* vt;       // [BH][n_b][d][64]  V blocks transposed (bf16 inputs only)
+  float* qbar;      // [BH][n_b][d]      block-mean queries (routing baselines only)
   double* s1_part;  // [BH][cov_parts][d]     (pre-pass scratch)
   double* s2_part;  // [BH][cov_parts][d][d]  (pre-pass scratch)
 };
 
 struct Layout {
-  size_t kbar_t, kbar, vsum, kmean, kcov, vt, s1_part, s2_part, total;
+  size_t kbar_t, kbar, vsum, kmean, kcov, vt, qbar, s1_part, s2_part, total;
 };
 
 Layout make_layout(const Shape& s);
@@ -70,10 +71,27 @@ struct FusedArgs {
   const uint64_t* mask_in;   // non-null: caller-given selection, no routing and no correction
 };
 
+// Routing baselines with a materialized proxy map (route.hip).
+enum RouteMode : int { kRouteThreshold = 0, kRouteTopK = 1, kRouteTopP = 2 };
+struct RouteArgs {
+  const void* q;
+  Workspace ws;        // pre-pass summaries of K (kbar) and room for qbar
+  int mode;
+  float beta;
+  int beta_mode;
+  int topk;
+  float topp;
+  float* proxy_map;    // [BH][n_b][n_b]
+  uint64_t* mask;      // [BH][n_b][n_words]
+  int32_t* kept;       // [BH][n_b] or null
+  int32_t* idx;        // [BH][n_b][topk] or null (top-k only)
+};
+
 // Each returns the first HIP error of its launches (hipSuccess otherwise).
 hipError_t launch_prepass(const Shape& s, Dtype dt, const void* k, const void* v,
                           const Workspace& ws, hipStream_t stream);
 hipError_t launch_fused(const Shape& s, Dtype dt, const FusedArgs& a, hipStream_t stream);
+hipError_t launch_route(const Shape& s, Dtype dt, const RouteArgs& a, hipStream_t stream);
 
 
 }  // namespace sol

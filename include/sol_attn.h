@@ -96,6 +96,7 @@ typedef struct sol_debug {
  *                         column c holding key 32*(c/32) + 4*g + s for
  *                         s = c%8 < 4, else 32*(c/32) + 16 + 4*g + s - 4,
  *                         with g = (c%32)/8 (written for bf16 inputs only)
+ *   qbar    [BH][n_b][d]  block-mean queries, written by sol_route only
  * the remaining bytes are scratch of the pre-pass. */
 typedef struct sol_workspace_layout {
   size_t total_bytes;
@@ -105,6 +106,7 @@ typedef struct sol_workspace_layout {
   size_t kmean;
   size_t kcov;
   size_t vt;
+  size_t qbar;
   size_t scratch;
 } sol_workspace_layout;
 
@@ -161,6 +163,40 @@ sol_status sol_attn_masked(const void* q, const void* k, const void* v, void* ou
                            int B, int H, int N, int d, const uint64_t* mask_bits,
                            unsigned flags, const void* workspace, size_t ws_bytes,
                            int32_t* kept_per_row, void* hip_stream);
+
+/* Routing baselines for the routing-cost and budget study: the proxy map
+ * s_hat = Q_bar K_bar^T / sqrt(d) of every head is materialized, then every
+ * row is selected by one of
+ *   SOL_ROUTE_THRESHOLD  s_hat_ij > mu_i + beta*sigma_i, mu_i and sigma_i the
+ *                        mean and population std of the materialized row
+ *                        (page "Sol-Attn: l'attenzione sparsa che sceglie al
+ *                        volo" (paithon.it), section "Una soglia per ogni riga");
+ *   SOL_ROUTE_TOPK       the row's top_k highest scores, ties to lower j;
+ *   SOL_ROUTE_TOPP       the best blocks (ties to lower j) until the softmax
+ *                        probability of the row's scores reaches top_p (the
+ *                        block that reaches it is kept; all if rounding never
+ *                        does); both from the same page, section "Perche
+ *                        l'attenzione pesa tanto nei video", which also says
+ *                        that both write the full score map and the chosen
+ *                        indices to GPU memory before attention starts.
+ * The fused pass never builds this map; sol_route exists to measure what it
+ * avoids. Needs the pre-pass workspace of the same K (sol_block_summaries);
+ * writes qbar into it.
+ *   q            device, [B][H][N][d] (bf16, or fp32 with SOL_F32)
+ *   proxy_map    device float [B*H*n_b*n_b], written (row-major per head)
+ *   mask_bits    device uint64 [B*H*n_b*W], written (layout of sol_debug.mask_bits)
+ *   kept_per_row device int32 [B*H*n_b] or NULL
+ *   topk_idx     device int32 [B*H*n_b*top_k] or NULL: SOL_ROUTE_TOPK only, the kept
+ *                key blocks of each row, best first (only min(top_k, n_b) written)
+ * flags: SOL_F32 and SOL_SYNC only. Errors: NaN beta / top_p or negative top_k,
+ * unknown mode -> SOL_ERR_INVALID_ARG. The masks feed sol_attn_masked. */
+#define SOL_ROUTE_THRESHOLD 0
+#define SOL_ROUTE_TOPK      1
+#define SOL_ROUTE_TOPP      2
+sol_status sol_route(const void* q, int B, int H, int N, int d, unsigned flags, int mode,
+                     float beta, int top_k, float top_p, const void* workspace, size_t ws_bytes,
+                     float* proxy_map, uint64_t* mask_bits, int32_t* kept_per_row,
+                     int32_t* topk_idx, void* hip_stream);
 
 /* Whole forward on a caller stream with a caller workspace:
  * sol_block_summaries followed by sol_attn_fused. Reentrant. */

@@ -85,7 +85,7 @@ def test_layout_offsets(lib):
     from free_block_sparse_mean_amd import binding
     lay = binding.sol_workspace_layout()
     assert lib.sol_attn_workspace_layout(2, 3, 64 * 100, 128, ctypes.byref(lay)) == 0
-    offs = [lay.kbar_t, lay.kbar, lay.vsum, lay.kmean, lay.kcov, lay.vt, lay.scratch]
+    offs = [lay.kbar_t, lay.kbar, lay.vsum, lay.kmean, lay.kcov, lay.vt, lay.qbar, lay.scratch]
     assert offs == sorted(offs) and offs[0] == 0 and lay.total_bytes > lay.scratch
     assert all(o % 256 == 0 for o in offs)
     assert lay.kbar - lay.kbar_t >= 6 * 128 * 100 * 4
@@ -101,3 +101,18 @@ def test_masked_validation(lib):
     assert lib.sol_attn_masked(p, p, p, p, 1, 1, 4096, 64, p, 0x4, p, 1 << 30, None, None) == 1
     assert lib.sol_attn_masked(p, p, p, p, 1, 1, 4096, 64, p, 0, p, 10, None, None) == 5
     assert lib.sol_attn_masked(p, p, p, p, 1, 1, 4096, 96, p, 0, p, 1 << 30, None, None) == 2
+
+
+def test_route_validation(lib):
+    """The routing entry point checks its arguments before any device call."""
+    p = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    big = 1 << 30
+    assert lib.sol_route(p, 1, 1, 4096, 64, 0, 0, 1.0, 0, 0.0, p, big, None, p, None, None, None) == 1
+    assert "proxy_map" in lib.sol_last_error().decode()
+    assert lib.sol_route(p, 1, 1, 4096, 64, 0, 7, 1.0, 0, 0.0, p, big, p, p, None, None, None) == 1
+    assert "mode" in lib.sol_last_error().decode()
+    assert lib.sol_route(p, 1, 1, 4096, 64, 0, 0, math.nan, 0, 0.0, p, big, p, p, None, None, None) == 1
+    assert lib.sol_route(p, 1, 1, 4096, 64, 0, 1, 0.0, -1, 0.0, p, big, p, p, None, None, None) == 1
+    assert lib.sol_route(p, 1, 1, 4096, 64, 0, 2, 0.0, 0, math.nan, p, big, p, p, None, None, None) == 1
+    assert lib.sol_route(p, 1, 1, 4096, 64, 0x2, 0, 1.0, 0, 0.0, p, big, p, p, None, None, None) == 1
+    assert lib.sol_route(p, 1, 1, 4096, 64, 0, 0, 1.0, 0, 0.0, p, 10, p, p, None, None, None) == 5

@@ -171,7 +171,8 @@ def select_topp(s_hat: np.ndarray, p: float) -> np.ndarray:
 
 
 def _attend_query_block(qi: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
-                        s_hat_row: np.ndarray, vbar: np.ndarray, correction: bool) -> np.ndarray:
+                        s_hat_row: np.ndarray, vbar: np.ndarray, correction: bool,
+                        kbar_rows: Optional[np.ndarray] = None) -> np.ndarray:
     """Output rows of one query block: exact tokens of kept blocks + virtual tokens.
 
     [IT] "Scegliere mentre si calcola", last paragraph: every token of an
@@ -179,6 +180,11 @@ def _attend_query_block(qi: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.n
     enters both the numerator and the denominator of the softmax; the logit
     reused is the block's proxy score. Form: 64 virtual tokens with logit
     s_hat_ij and value v_bar_j per unselected block j.
+
+    With kbar_rows (the float64 block-mean keys) the virtual tokens of row r
+    take the per-row logit q_r . k_bar_j / sqrt(d) instead: the literal reading
+    of "each token takes the block-mean key" (exact when a block's 64 keys are
+    equal), which the pages leave beside the block-level reuse.
     """
     d = qi.shape[1]
     kept = np.flatnonzero(keep)
@@ -189,28 +195,32 @@ def _attend_query_block(qi: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.n
     v_kept = vb[kept].reshape(-1, d)
 
     logits = (qi @ k_kept.T) / math.sqrt(d)                 # [64, 64*|S_i|]
-    if correction and dropped.size:
-        virt = np.asarray(s_hat_row[dropped], dtype=np.float64)   # [n_drop]
-    else:
-        virt = np.zeros((0,), dtype=np.float64)
-
     rows = qi.shape[0]
+    if correction and dropped.size:
+        if kbar_rows is None:                                 # block-level logit, same for every row
+            virt = np.broadcast_to(np.asarray(s_hat_row[dropped], dtype=np.float64)[None, :],
+                                   (rows, dropped.size))
+        else:                                                 # per-row logit
+            virt = (qi @ kbar_rows[dropped].T) / math.sqrt(d)
+    else:
+        virt = np.zeros((rows, 0), dtype=np.float64)
+
     out = np.zeros((rows, d), dtype=np.float64)
-    if logits.shape[1] == 0 and virt.size == 0:
+    if logits.shape[1] == 0 and virt.shape[1] == 0:
         return out                                             # nothing to attend to
     row_max = np.full(rows, -np.inf)
     if logits.shape[1]:
         row_max = logits.max(axis=1)
-    if virt.size:
-        row_max = np.maximum(row_max, virt.max())
+    if virt.shape[1]:
+        row_max = np.maximum(row_max, virt.max(axis=1))
     num = np.zeros((rows, d))
     den = np.zeros(rows)
     if logits.shape[1]:
         p = np.exp(logits - row_max[:, None])
         num += p @ v_kept
         den += p.sum(axis=1)
-    if virt.size:
-        w = BLOCK * np.exp(virt[None, :] - row_max[:, None])  # [64, n_drop]
+    if virt.shape[1]:
+        w = BLOCK * np.exp(virt - row_max[:, None])            # [64, n_drop]
         num += w @ vbar[dropped]
         den += w.sum(axis=1)
     return num / den[:, None]
@@ -220,7 +230,8 @@ def sol_attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: float,
                        correction: bool = True, *,
                        query_blocks: Optional[Sequence[int]] = None,
                        mask_override: Optional[np.ndarray] = None,
-                       route_dtype=np.float32) -> Dict[str, np.ndarray]:
+                       route_dtype=np.float32,
+                       correction_form: str = "block") -> Dict[str, np.ndarray]:
     """Sol-Attn forward for one head. q, k, v: [N, d] (any float dtype; upcast to float64).
 
     Returns a dict with
@@ -231,7 +242,11 @@ def sol_attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: float,
     mask_override, if given ([len(query_blocks), n_b] bool), replaces S_i for the
     attention step (routing quantities are still returned), so that arithmetic
     can be compared separately from the selection.
+    correction_form: "block" (the logit of a block's virtual tokens is s_hat_ij)
+    or "row" (q_r . k_bar_j / sqrt(d) for row r, see _attend_query_block).
     """
+    if correction_form not in ("block", "row"):
+        raise ValueError("correction_form must be 'block' or 'row'")
     q64 = np.asarray(q, dtype=np.float64)
     k64 = np.asarray(k, dtype=np.float64)
     v64 = np.asarray(v, dtype=np.float64)
@@ -248,11 +263,13 @@ def sol_attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: float,
     mask = select_blocks(s_hat, tau)
     use = mask if mask_override is None else np.asarray(mask_override, dtype=bool)
 
+    kbar_rows = block_means(k64) if correction_form == "row" else None
     out = np.empty((qb.size * BLOCK, d), dtype=np.float64)
     for r, i in enumerate(qb):
         qi = q64[i * BLOCK:(i + 1) * BLOCK]
         out[r * BLOCK:(r + 1) * BLOCK] = _attend_query_block(
-            qi, k64, v64, use[r], s_hat[r], vbar, correction)
+            qi, k64, v64, use[r], s_hat[r], vbar, correction,
+            kbar_rows=kbar_rows)
     return {"out": out, "mask": mask, "s_hat": s_hat, "mu": mu, "sigma": sigma,
             "tau": tau, "kept": mask.sum(axis=1)}
 

@@ -419,3 +419,50 @@ def test_topk_topp_monotone():
         cur = orc.select_topp(s, p)
         assert (cur >= prev).all()
         prev = cur
+
+
+# ---- per-row correction logit ----------------------------------------------
+
+@pytest.mark.parametrize("beta", [-0.3, 0.4, 1.2, math.inf])
+def test_row_correction_exact_for_constant_key_blocks(beta):
+    """Per-row form: if the 64 keys of every key block are equal, each virtual token is the
+    real token, so the corrected output equals dense attention for any beta, whatever the
+    queries ([IT] 'Scegliere mentre si calcola': every token of an excluded block takes the
+    block-mean key). The block-level form is not exact here (its logit ignores q_r - q_bar_i)."""
+    rng = _rng(70)
+    nb, d = 9, 16
+    q = rng.standard_normal((nb * BLK, d)) + np.repeat(rng.standard_normal((nb, d)), BLK, axis=0)
+    k = np.repeat(rng.standard_normal((nb, d)), BLK, axis=0)
+    v = rng.standard_normal((nb * BLK, d))
+    dense = orc.dense_attention(q, k, v)
+    r = orc.sol_attention_head(q, k, v, beta, True, route_dtype=np.float64, correction_form="row")
+    np.testing.assert_allclose(r["out"], dense, rtol=1e-11, atol=1e-12)
+    if beta != -0.3:
+        blk = orc.sol_attention_head(q, k, v, beta, True, route_dtype=np.float64)
+        assert np.abs(blk["out"] - dense).max() > 1e-6
+
+
+def test_row_correction_equals_block_for_constant_query_blocks():
+    """With constant query blocks q_r = q_bar_i, the per-row logit is the block proxy."""
+    rng = _rng(71)
+    nb, d = 7, 8
+    q = np.repeat(rng.standard_normal((nb, d)), BLK, axis=0)
+    k = rng.standard_normal((nb * BLK, d))
+    v = rng.standard_normal((nb * BLK, d))
+    for beta in (0.0, 0.8):
+        a = orc.sol_attention_head(q, k, v, beta, True, route_dtype=np.float64, correction_form="row")
+        b = orc.sol_attention_head(q, k, v, beta, True, route_dtype=np.float64)
+        np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-13)
+
+
+def test_row_correction_only_is_attention_over_summaries():
+    """beta = +inf with the per-row correction: each row attends to the block summaries
+    (k_bar_j, v_bar_j), the multiplicity 64 cancelling: dense attention of q_r over them."""
+    rng = _rng(72)
+    nb, d = 6, 5
+    q, k, v = (rng.standard_normal((nb * BLK, d)) for _ in range(3))
+    r = orc.sol_attention_head(q, k, v, math.inf, True, route_dtype=np.float64, correction_form="row")
+    kb, vb = orc.block_means(k), orc.block_means(v)
+    np.testing.assert_allclose(r["out"], orc.dense_attention(q, kb, vb), rtol=1e-11, atol=1e-12)
+    with pytest.raises(ValueError):
+        orc.sol_attention_head(q, k, v, 1.0, True, correction_form="tokens")

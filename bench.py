@@ -329,6 +329,7 @@ def main() -> int:
     rows = row_stats(kept)
     balance = load_balance(sb, qd, kd, vd, out, ws, args.beta, corr, w)
     ablation = routing_overhead(sb, qd, kd, vd, out, ws, args.beta, w, max(3, args.steps // 2))
+    rowc = None if args.no_correction else measure(args.beta, sb.SOL_CORRECTION_ROW, max(3, args.steps // 2), 1)
     study = None if args.no_routing_study else routing_study(sb, qd, kd, vd, out, ws, w, 5)
     # the two-call step equals one sol_attn_fwd_ex call (bit for bit)
     ref = out.clone()
@@ -382,6 +383,7 @@ def main() -> int:
         "kept_per_row": rows,
         "load_balance": balance,
         "routing_ablation": ablation,
+        "row_correction": rowc,
         "routing_study": study,
         "prepass": {"ms": head["prepass_ms"], "hbm_gbs": head["prepass_hbm_gbs"],
                     "frac": head["prepass_hbm_gbs"] / PEAK_HBM_GBS},

@@ -29,6 +29,7 @@ SOL_F32 = 0x1
 SOL_CORRECTION = 0x2
 SOL_DENSE = 0x4
 SOL_SYNC = 0x8
+SOL_CORRECTION_ROW = 0x10
 
 SOL_ROUTE_THRESHOLD = 0
 SOL_ROUTE_TOPK = 1
@@ -52,7 +53,8 @@ class sol_debug(ctypes.Structure):
 
 class sol_workspace_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("total_bytes", "kbar_t", "kbar", "vsum", "kmean", "kcov", "vt", "qbar", "scratch")]
+                ("total_bytes", "kbar_t", "kbar", "vsum", "kmean", "kcov", "vt", "qbar", "kbar_bf",
+                  "vbar_t", "scratch")]
 
 
 _lib = None

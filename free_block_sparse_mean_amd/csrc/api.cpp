@@ -27,6 +27,8 @@ Layout make_layout(const Shape& s) {
   L.kcov = off;     off += up256(bh * d * d * 4);
   L.vt = off;       off += up256(bh * nb * d * 64 * 2);
   L.qbar = off;     off += up256(bh * nb * d * 4);
+  L.kbar_bf = off;  off += up256(bh * (size_t)s.n_words * 64 * d * 2);
+  L.vbar_t = off;   off += up256(bh * (size_t)s.n_words * 64 * d * 2);
   L.s1_part = off;  off += up256(bh * (size_t)s.cov_parts * d * 8);
   L.s2_part = off;  off += up256(bh * (size_t)s.cov_parts * d * d * 8);
   L.total = off;
@@ -44,6 +46,8 @@ Workspace bind_workspace(const Shape& s, void* base) {
   w.kcov = reinterpret_cast<float*>(b + L.kcov);
   w.vt = reinterpret_cast<__bf16*>(b + L.vt);
   w.qbar = reinterpret_cast<float*>(b + L.qbar);
+  w.kbar_bf = reinterpret_cast<__bf16*>(b + L.kbar_bf);
+  w.vbar_t = reinterpret_cast<__bf16*>(b + L.vbar_t);
   w.s1_part = reinterpret_cast<double*>(b + L.s1_part);
   w.s2_part = reinterpret_cast<double*>(b + L.s2_part);
   return w;
@@ -128,7 +132,8 @@ sol_status fused_checked(const sol::Shape& s, const void* q, const void* k, cons
   a.beta_mode = (flags & SOL_DENSE) || beta == -INFINITY ? sol::kBetaMinusInf
                 : beta == INFINITY                       ? sol::kBetaPlusInf
                                                          : sol::kBetaFinite;
-  a.correction = (flags & SOL_CORRECTION) != 0;
+  a.correction = (flags & (SOL_CORRECTION | SOL_CORRECTION_ROW)) != 0;
+  a.correction_row = (flags & SOL_CORRECTION_ROW) != 0;
   a.kept_per_row = dbg ? dbg->kept_per_row : nullptr;
   a.mask_bits = dbg ? dbg->mask_bits : nullptr;
   a.tau = dbg ? dbg->tau : nullptr;
@@ -187,6 +192,8 @@ sol_status sol_attn_workspace_layout(int B, int H, int N, int d, sol_workspace_l
   layout->kcov = L.kcov;
   layout->vt = L.vt;
   layout->qbar = L.qbar;
+  layout->kbar_bf = L.kbar_bf;
+  layout->vbar_t = L.vbar_t;
   layout->scratch = L.s1_part;
   return ok();
 }
@@ -231,8 +238,8 @@ sol_status sol_attn_masked(const void* q, const void* k, const void* v, void* ou
   if (!q || !k || !v || !out || !mask_bits)
     return fail(SOL_ERR_INVALID_ARG, "q, k, v, out and mask_bits must be non-null");
   if ((st = check_flags(flags)) != SOL_OK) return st;
-  if (flags & (SOL_CORRECTION | SOL_DENSE))
-    return fail(SOL_ERR_INVALID_ARG, "the given-mask mode takes neither SOL_CORRECTION nor SOL_DENSE");
+  if (flags & (SOL_CORRECTION | SOL_CORRECTION_ROW | SOL_DENSE))
+    return fail(SOL_ERR_INVALID_ARG, "the given-mask mode takes neither SOL_CORRECTION(_ROW) nor SOL_DENSE");
   if (!workspace || ws_bytes < sol::make_layout(s).total)
     return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
                 ws_bytes, workspace ? "" : ", NULL");
@@ -243,6 +250,7 @@ sol_status sol_attn_masked(const void* q, const void* k, const void* v, void* ou
   a.beta = 0.f;
   a.beta_mode = sol::kBetaFinite;
   a.correction = false;
+  a.correction_row = false;
   a.kept_per_row = kept_per_row;
   a.mask_bits = nullptr;
   a.tau = nullptr;
@@ -263,8 +271,8 @@ sol_status sol_route(const void* q, int B, int H, int N, int d, unsigned flags, 
   if (!q || !proxy_map || !mask_bits)
     return fail(SOL_ERR_INVALID_ARG, "q, proxy_map and mask_bits must be non-null");
   if ((st = check_flags(flags)) != SOL_OK) return st;
-  if (flags & (SOL_CORRECTION | SOL_DENSE))
-    return fail(SOL_ERR_INVALID_ARG, "routing takes neither SOL_CORRECTION nor SOL_DENSE");
+  if (flags & (SOL_CORRECTION | SOL_CORRECTION_ROW | SOL_DENSE))
+    return fail(SOL_ERR_INVALID_ARG, "routing takes neither SOL_CORRECTION(_ROW) nor SOL_DENSE");
   if (mode != SOL_ROUTE_THRESHOLD && mode != SOL_ROUTE_TOPK && mode != SOL_ROUTE_TOPP)
     return fail(SOL_ERR_INVALID_ARG, "unknown routing mode %d", mode);
   if (mode == SOL_ROUTE_THRESHOLD && isnan(beta)) return fail(SOL_ERR_INVALID_ARG, "beta is NaN");

@@ -61,6 +61,9 @@ struct FusedParams {
   const void* v;
   void* out;
   const __bf16* vt;
+  const __bf16* kbar_bf;   // block-summary tiles for the per-row correction (bf16)
+  const __bf16* vbar_t;
+  const float* kbar;       // block means (fp32 per-row correction)
   const float* kbar_t;
   const float* vsum;
   const float* kmean;
@@ -243,11 +246,11 @@ __device__ __forceinline__ DmaLane dma_lane(int t) {
 // straight into LDS buffer `buf`. Completion is awaited with s_waitcnt vmcnt
 // before the next barrier.
 template <int D>
-__device__ __forceinline__ void issue_tile(unsigned char* buf, const __bf16* Kh, const __bf16* Vt,
-                                           long long bh, int n_b, int j, const DmaLane& dl) {
+__device__ __forceinline__ void issue_tile(unsigned char* buf, const __bf16* Ksrc, const __bf16* Vsrc,
+                                           const DmaLane& dl) {
   constexpr int NI = D / 32;   // slabs per region
-  const unsigned char* Kj = reinterpret_cast<const unsigned char*>(Kh + (size_t)j * kBlock * D);
-  const unsigned char* Vj = reinterpret_cast<const unsigned char*>(Vt + ((size_t)bh * n_b + j) * D * 64);
+  const unsigned char* Kj = reinterpret_cast<const unsigned char*>(Ksrc);   // [64][D]
+  const unsigned char* Vj = reinterpret_cast<const unsigned char*>(Vsrc);   // [D][64]
 #pragma unroll
   for (int i = 0; i < NI; ++i)
     __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(Kj + dl.k_off + i * 4096),
@@ -294,10 +297,16 @@ template <int D> struct LaneOfs {
 
 // One tile of 64 keys for one query block of this wave: S^T = K Q^T, online
 // softmax in base 2, O^T += V^T P^T.
-template <int D>
-__device__ __forceinline__ void tile_bf16(ExactState<__bf16, D>& st, const unsigned char* buf, const LaneOfs<D>& lo) {
+// VIRT: a tile of block summaries (per-row correction): the 64 "keys" are the
+// block means k_bar_j of 64 key blocks, each standing for 64 equal tokens
+// (base-2 logit + log2(64) = 6), values v_bar_j; key blocks whose bit is set
+// in `excl` (kept exactly, or past n_b) get weight zero.
+template <int D, bool VIRT = false>
+__device__ __forceinline__ void tile_bf16(ExactState<__bf16, D>& st, const unsigned char* buf, const LaneOfs<D>& lo,
+                                          uint64_t excl = 0) {
   using S = ExactState<__bf16, D>;
   constexpr float kScale2 = inv_sqrt(D) * kLog2e;   // logit -> base-2 exponent
+  constexpr float kOff = VIRT ? 6.0f : 0.0f;        // log2 of the multiplicity
   // S^T (64 keys x 16 queries): 4 key sub-tiles of 16 rows of D/8 chunks
   // (16*D*2 bytes apart). K-step outer, sub-tile inner: four independent
   // accumulation chains, and the operands of k-step ks+1 are read while the
@@ -320,6 +329,20 @@ __device__ __forceinline__ void tile_bf16(ExactState<__bf16, D>& st, const unsig
     for (int kt = 0; kt < 4; ++kt)
       s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks & 1][kt], st.qop[ks], s[kt], 0, 0, 0);
   }
+  if constexpr (VIRT) {
+    // the lane's 16 keys are 16kt + 4*(lane/16) + i: gather their exclusion
+    // bits into one 16-bit lane mask (excl is uniform, in scalar registers)
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)excl);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(excl >> 32));
+    const int sh = 4 * ((threadIdx.x & 63) >> 4);
+    const uint32_t m16 = ((lo >> sh) & 0xFu) | (((lo >> (16 + sh)) & 0xFu) << 4) |
+                         (((hi >> sh) & 0xFu) << 8) | (((hi >> (16 + sh)) & 0xFu) << 12);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((m16 >> (4 * kt + i)) & 1u) s[kt][i] = -INFINITY;
+  }
   // Online softmax: the lane holds keys 16kt + (lane/16)*4 + i of its query
   // row. A row's reference moves only when the tile maximum exceeds it by the
   // slack. Each lane first tests its own 16 values; only when some lane of
@@ -330,7 +353,7 @@ __device__ __forceinline__ void tile_bf16(ExactState<__bf16, D>& st, const unsig
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, s[kt][i]);
-  lmax *= kScale2;
+  lmax = lmax * kScale2 + kOff;
   if (__ballot(lmax > st.mrow + kRescaleSlack)) {
     const float tmax = quad16_max(lmax);
     const bool grow = tmax > st.mrow + kRescaleSlack;
@@ -347,7 +370,7 @@ __device__ __forceinline__ void tile_bf16(ExactState<__bf16, D>& st, const unsig
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      pop[kt >> 1][(kt & 1) * 4 + i] = to_bf16(fast_exp2(__builtin_fmaf(s[kt][i], kScale2, -mref)));
+      pop[kt >> 1][(kt & 1) * 4 + i] = to_bf16(fast_exp2(__builtin_fmaf(s[kt][i], kScale2, kOff - mref)));
   // the row sum adds the bf16 weights that enter the P V product, two per
   // dot2 instruction (products by 1 are exact, accumulation in fp32)
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -374,11 +397,13 @@ __device__ __forceinline__ void tile_bf16(ExactState<__bf16, D>& st, const unsig
 // One tile of 64 keys for one query block, fp32: 4 lanes per query row, each
 // a quarter of the head dims; dot products and the weighted sum of V on the
 // VALU from LDS-staged K and V; online softmax in base 2.
-template <int D>
-__device__ __forceinline__ void tile_f32(ExactState<float, D>& st, const unsigned char* buf, int lane) {
+template <int D, bool VIRT = false>
+__device__ __forceinline__ void tile_f32(ExactState<float, D>& st, const unsigned char* buf, int lane,
+                                         uint64_t excl = 0) {
   using S = ExactState<float, D>;
   using Gm = Geom<float, D>;
   constexpr float kScale2 = inv_sqrt(D) * kLog2e;   // logit -> base-2 exponent
+  constexpr float kOff = VIRT ? 6.0f : 0.0f;        // log2 of the multiplicity (block summaries)
   const int grp = lane >> 4;
   {
     const float* stK = reinterpret_cast<const float*>(buf);
@@ -393,7 +418,7 @@ __device__ __forceinline__ void tile_f32(ExactState<float, D>& st, const unsigne
       for (int e = 0; e < S::NF; ++e) a += st.qf[e] * kr[e];
       a += __shfl_xor(a, 16, 64);
       a += __shfl_xor(a, 32, 64);
-      sv[key] = a * kScale2;
+      sv[key] = (VIRT && ((excl >> key) & 1ull)) ? -INFINITY : a * kScale2 + kOff;
       tmax = fmaxf(tmax, sv[key]);
     }
     const float mnew = fmaxf(st.mrow, tmax);
@@ -458,9 +483,11 @@ __device__ __forceinline__ void epilogue(ExactState<T, D>& st, const FusedParams
   }
 }
 
-// Kernel modes: routing without / with the correction, or a caller-given
-// block mask (plain block-sparse attention: no routing, no correction).
-constexpr int kModeRoute = 0, kModeCorr = 1, kModeGiven = 2;
+// Kernel modes: routing without / with the correction (block-level logit), a
+// caller-given block mask (plain block-sparse attention: no routing, no
+// correction), or routing with the per-row correction logit (the unselected
+// blocks enter as tiles of block summaries in the walk).
+constexpr int kModeRoute = 0, kModeCorr = 1, kModeGiven = 2, kModeCorrRow = 3;
 
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel(FusedParams p) {
@@ -760,6 +787,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       return -1;
     };
+    const __bf16* Vt = p.vt + (size_t)bh * n_b * D * 64;
 // s_waitcnt vmcnt(0) through the builtin, so the compiler's own wait tracking
 // knows the tile loads have landed (gfx9 encoding: vmcnt in bits 3:0, expcnt
 // 6:4 and lgkmcnt 11:8 left at their maxima)
@@ -777,17 +805,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       asm volatile("" ::: "memory");                                              \
       __builtin_amdgcn_s_barrier();                                               \
       asm volatile("" ::: "memory");                                              \
-      if (nj >= 0) issue_tile<D>(NEXTB, Kh, p.vt, bh, n_b, nj, dl);               \
-      _Pragma("unroll") for (int g = 0; g < kGMax; ++g)                          \
+      if (nj >= 0)                                                                \
+        issue_tile<D>(NEXTB, Kh + (size_t)nj * kBlock * D, Vt + (size_t)nj * D * 64, dl); \
+      _Pragma("unroll") for (int g = 0; g < kGMax; ++g)                           \
         if (keep & (1u << g)) tile_bf16<D>(sts[g], CURB, lofs);                   \
       j = nj;                                                                     \
     }
     int j = union_next(-1);
-    if (j >= 0) issue_tile<D>(sbufA, Kh, p.vt, bh, n_b, j, dl);
+    if (j >= 0) issue_tile<D>(sbufA, Kh + (size_t)j * kBlock * D, Vt + (size_t)j * D * 64, dl);
     while (j >= 0) {
       SOL_STEP(sbufA, sbufB)
       if (j < 0) break;
       SOL_STEP(sbufB, sbufA)
+    }
+    if constexpr (MODE == kModeCorrRow) {
+      // Per-row correction: the n_words tiles of block summaries (k_bar_j and
+      // v_bar_j of 64 key blocks each) go through the same online softmax,
+      // every block of the group taking the key blocks it did not keep.
+      const __bf16* Kbs = p.kbar_bf + (size_t)bh * n_words * 64 * D;
+      const __bf16* Vbs = p.vbar_t + (size_t)bh * n_words * D * 64;
+      SOL_WAIT_VM();   // both buffers free: every load landed, every wave past its last tile
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue_tile<D>(sbufA, Kbs, Vbs, dl);
+#define SOL_VSTEP(CURB, NEXTB)                                                    \
+      {                                                                           \
+        const uint64_t pad = (c == n_words - 1 && (n_b & 63)) ? ~0ull << (n_b & 63) : 0ull; \
+        SOL_WAIT_VM();                                                            \
+        asm volatile("" ::: "memory");                                            \
+        __builtin_amdgcn_s_barrier();                                             \
+        asm volatile("" ::: "memory");                                            \
+        if (c + 1 < n_words)                                                      \
+          issue_tile<D>(NEXTB, Kbs + (size_t)(c + 1) * 64 * D, Vbs + (size_t)(c + 1) * D * 64, dl); \
+        _Pragma("unroll") for (int g = 0; g < kGMax; ++g) {                       \
+          const uint64_t ex = g < nG ? (masks[g * n_words + c] | pad) : ~0ull;    \
+          if (ex != ~0ull) tile_bf16<D, true>(sts[g], CURB, lofs, ex);            \
+        }                                                                         \
+        ++c;                                                                      \
+      }
+      int c = 0;
+      while (true) {
+        SOL_VSTEP(sbufA, sbufB)
+        if (c >= n_words) break;
+        SOL_VSTEP(sbufB, sbufA)
+        if (c >= n_words) break;
+      }
+#undef SOL_VSTEP
     }
 #undef SOL_STEP
 #undef SOL_WAIT_VM
@@ -814,6 +878,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           tile_f32<D>(st, sbufA, lane);
         }
       }
+      if constexpr (MODE == kModeCorrRow) {
+        // per-row correction: tiles of block summaries (k_bar_j, v_bar_j) of
+        // 64 key blocks each; kept blocks and blocks past n_b get no weight
+        using Gm2 = Geom<float, D>;
+        float* stK = reinterpret_cast<float*>(sbufA);
+        float* stV = reinterpret_cast<float*>(sbufA + Gm2::kKBytes);
+        for (int c = 0; c < n_words; ++c) {
+          const uint64_t pad = (c == n_words - 1 && (n_b & 63)) ? ~0ull << (n_b & 63) : 0ull;
+          const uint64_t ex = masks[g * n_words + c] | pad;
+          if (ex == ~0ull) continue;   // uniform over the workgroup
+          __syncthreads();
+          for (int e = t; e < 64 * (D / 4); e += 256) {
+            const int r = e / (D / 4), cc = e % (D / 4), jj = 64 * c + r;
+            float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+            if (jj < n_b) {
+              kx = reinterpret_cast<const float4*>(p.kbar + ((size_t)bh * n_b + jj) * D)[cc];
+              vx = reinterpret_cast<const float4*>(p.vsum + ((size_t)bh * n_b + jj) * D)[cc];
+            }
+            const float sc = 1.0f / kBlock;   // v_bar = vsum / 64, exact
+            *reinterpret_cast<float4*>(stK + r * Gm2::kKPitch + cc * 4) = kx;
+            *reinterpret_cast<float4*>(stV + r * Gm2::kVPitch + cc * 4) =
+                make_float4(vx.x * sc, vx.y * sc, vx.z * sc, vx.w * sc);
+          }
+          __syncthreads();
+          tile_f32<D, true>(st, sbufA, lane, ex);
+        }
+      }
       epilogue<T, D>(st, p, bh, qi0 + g, g, row, lane, qa, misc);
     }
   }
@@ -834,6 +925,9 @@ hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
   FusedParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.out = a.out;
   p.vt = a.ws.vt;
+  p.kbar_bf = a.ws.kbar_bf;
+  p.vbar_t = a.ws.vbar_t;
+  p.kbar = a.ws.kbar;
   p.kbar_t = a.ws.kbar_t; p.vsum = a.ws.vsum; p.kmean = a.ws.kmean; p.kcov = a.ws.kcov;
   p.n_b = s.n_b; p.n_b_pad = s.n_b_pad; p.n_words = s.n_words;
   p.G = g.G; p.n_groups = g.n_groups; p.BH = s.BH(); p.per_xcd = g.per_xcd;
@@ -843,9 +937,10 @@ hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
   p.item_clock = a.item_clock;
   p.mask_in = a.mask_in;
   const dim3 grid((unsigned)(8 * g.per_xcd * s.BH()));
-  const void* fn = a.mask_in      ? (const void*)fused_kernel<T, D, kModeGiven>
-                   : a.correction ? (const void*)fused_kernel<T, D, kModeCorr>
-                                  : (const void*)fused_kernel<T, D, kModeRoute>;
+  const void* fn = a.mask_in          ? (const void*)fused_kernel<T, D, kModeGiven>
+                   : a.correction_row ? (const void*)fused_kernel<T, D, kModeCorrRow>
+                   : a.correction     ? (const void*)fused_kernel<T, D, kModeCorr>
+                                      : (const void*)fused_kernel<T, D, kModeRoute>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
   if (e != hipSuccess) return e;
   void* args[] = {&p};

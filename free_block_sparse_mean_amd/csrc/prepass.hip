@@ -203,6 +203,31 @@ __global__ __launch_bounds__(256) void moments_reduce_kernel(const double* __res
   kcov[(size_t)bh * D * D + e] = (float)(s / (double)n_b - m[e / D] * m[e % D]);
 }
 
+// Block summaries as bf16 MFMA tiles, for the per-row correction: chunk c of
+// 64 key blocks gives a K-like tile [64][D] of k_bar_j and a V^T-like tile
+// [D][64] of v_bar_j = vsum_j / 64 in the column order of the V^T tiles; rows
+// and columns past n_b are zero (the fused pass masks them out).
+template <int D>
+__global__ __launch_bounds__(256) void virtual_tiles_kernel(const float* __restrict__ kbar,
+                                                            const float* __restrict__ vsum,
+                                                            __bf16* __restrict__ kbar_bf,
+                                                            __bf16* __restrict__ vbar_t, int n_b,
+                                                            int n_chunks) {
+  const int c = blockIdx.x, t = threadIdx.x;
+  const long long bh = blockIdx.y;
+  __bf16* kd = kbar_bf + ((size_t)bh * n_chunks + c) * 64 * D;
+  for (int e = t; e < 64 * D; e += 256) {
+    const int r = e / D, dd = e % D, j = 64 * c + r;
+    kd[e] = j < n_b ? to_bf16(kbar[((size_t)bh * n_b + j) * D + dd]) : to_bf16(0.f);
+  }
+  __bf16* vd = vbar_t + ((size_t)bh * n_chunks + c) * D * 64;
+  for (int e = t; e < D * 64; e += 256) {
+    const int dd = e / 64, col = e % 64, kc = col / 8, ee = col % 8;
+    const int j = 64 * c + 32 * (kc >> 2) + 4 * (kc & 3) + 16 * (ee >> 2) + (ee & 3);
+    vd[e] = j < n_b ? to_bf16(vsum[((size_t)bh * n_b + j) * D + dd] * (1.0f / kBlock)) : to_bf16(0.f);
+  }
+}
+
 template <typename T, int D>
 hipError_t prepass_impl(const Shape& s, const void* k, const void* v, const Workspace& ws,
                         hipStream_t st) {
@@ -216,6 +241,11 @@ hipError_t prepass_impl(const Shape& s, const void* k, const void* v, const Work
   hipLaunchKernelGGL((moments_partial_kernel<D>), dim3(s.cov_parts, bh), dim3(256), 0, st, ws.kbar,
                      ws.kbar_t, ws.s1_part, ws.s2_part, s.n_b, s.n_b_pad, s.cov_parts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if constexpr (kVT) {
+    hipLaunchKernelGGL((virtual_tiles_kernel<D>), dim3(s.n_words, bh), dim3(256), 0, st, ws.kbar, ws.vsum,
+                       ws.kbar_bf, ws.vbar_t, s.n_b, s.n_words);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((moments_reduce_kernel<D>), dim3((D * D + 255) / 256, bh), dim3(256), 0, st,
                      ws.s1_part, ws.s2_part, ws.kmean, ws.kcov, s.n_b, s.cov_parts);
   return hipGetLastError();

@@ -34,12 +34,14 @@ struct Workspace {
   float* kcov;      // [BH][d][d]
   __bf16* vt;       // [BH][n_b][d][64]  V blocks transposed (bf16 inputs only)
   float* qbar;      // [BH][n_b][d]      block-mean queries (routing baselines only)
+  __bf16* kbar_bf;  // [BH][n_words][64][d]  k_bar as bf16 tiles (per-row correction; bf16 only)
+  __bf16* vbar_t;   // [BH][n_words][d][64]  v_bar as bf16 V^T-order tiles (per-row correction)
   double* s1_part;  // [BH][cov_parts][d]     (pre-pass scratch)
   double* s2_part;  // [BH][cov_parts][d][d]  (pre-pass scratch)
 };
 
 struct Layout {
-  size_t kbar_t, kbar, vsum, kmean, kcov, vt, qbar, s1_part, s2_part, total;
+  size_t kbar_t, kbar, vsum, kmean, kcov, vt, qbar, kbar_bf, vbar_t, s1_part, s2_part, total;
 };
 
 Layout make_layout(const Shape& s);
@@ -64,6 +66,7 @@ struct FusedArgs {
   float beta;
   int beta_mode;
   bool correction;
+  bool correction_row;   // per-row correction logit q_r . k_bar_j (instead of s_hat_ij)
   int32_t* kept_per_row;
   uint64_t* mask_bits;
   float* tau;

@@ -65,7 +65,10 @@ typedef enum sol_status {
 #define SOL_CORRECTION 0x2u  /* fold every unselected block in as 64 virtual tokens         */
 #define SOL_DENSE      0x4u  /* keep every block (same selection as beta = -INFINITY)       */
 #define SOL_SYNC       0x8u  /* synchronise the stream before returning, report its errors  */
-#define SOL_FLAGS_ALL  0xFu
+#define SOL_CORRECTION_ROW 0x10u /* correction with the per-row logit q_r . k_bar_j / sqrt(d)
+                                    of every virtual token, instead of the block proxy
+                                    s_hat_ij (implies SOL_CORRECTION)                         */
+#define SOL_FLAGS_ALL  0x1Fu
 
 /* Optional per-call outputs, all device pointers owned by the caller, each may be NULL.
  * n_b = N / 64, W = ceil(n_b / 64).
@@ -97,6 +100,11 @@ typedef struct sol_debug {
  *                         s = c%8 < 4, else 32*(c/32) + 16 + 4*g + s - 4,
  *                         with g = (c%32)/8 (written for bf16 inputs only)
  *   qbar    [BH][n_b][d]  block-mean queries, written by sol_route only
+ *   kbar_bf [BH][W][64][d] bfloat16: k_bar_j of key blocks 64c .. 64c+63 as
+ *                         tile c (zero past n_b), for SOL_CORRECTION_ROW
+ *   vbar_t  [BH][W][d][64] bfloat16: v_bar_j of the same blocks, transposed,
+ *                         columns in the vt key order (zero past n_b)
+ *                         (both written by the pre-pass for bf16 inputs)
  * the remaining bytes are scratch of the pre-pass. */
 typedef struct sol_workspace_layout {
   size_t total_bytes;
@@ -107,6 +115,8 @@ typedef struct sol_workspace_layout {
   size_t kcov;
   size_t vt;
   size_t qbar;
+  size_t kbar_bf;
+  size_t vbar_t;
   size_t scratch;
 } sol_workspace_layout;
 

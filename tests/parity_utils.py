@@ -49,7 +49,8 @@ def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
 
 def check_head(qh, kh, vh, gpu_out_h: np.ndarray, gpu_mask_h: np.ndarray, gpu_tau_h: np.ndarray,
                beta: float, correction: bool, dtype: str,
-               query_blocks: Optional[Sequence[int]] = None, label: str = "") -> Dict[str, float]:
+               query_blocks: Optional[Sequence[int]] = None, label: str = "",
+               correction_form: str = "block") -> Dict[str, float]:
     """Compare one head of the HIP result with the oracle.
 
     qh, kh, vh: host tensors [N, d] (bf16 or f32) - the exact values the GPU read.
@@ -63,7 +64,8 @@ def check_head(qh, kh, vh, gpu_out_h: np.ndarray, gpu_mask_h: np.ndarray, gpu_ta
     v = vh.float().numpy()
     nb = q.shape[0] // BLK
     qb = np.arange(nb) if query_blocks is None else np.asarray(query_blocks)
-    ref = orc.sol_attention_head(q, k, v, beta, correction, query_blocks=qb)
+    ref = orc.sol_attention_head(q, k, v, beta, correction, query_blocks=qb,
+                                 correction_form=correction_form)
     gmask = gpu_mask_h[qb]
     diff = ref["mask"] != gmask
     n_flip = int(diff.sum())
@@ -78,7 +80,8 @@ def check_head(qh, kh, vh, gpu_out_h: np.ndarray, gpu_mask_h: np.ndarray, gpu_ta
     rows = (qb[:, None] * BLK + np.arange(BLK)[None, :]).ravel()
     got = gpu_out_h[rows]
     rel_tol, abs_tol = (BF16_REL_L2, BF16_MAX_ABS) if dtype == "bf16" else (F32_REL_L2, F32_MAX_ABS)
-    arith = orc.sol_attention_head(q, k, v, beta, correction, query_blocks=qb, mask_override=gmask)
+    arith = orc.sol_attention_head(q, k, v, beta, correction, query_blocks=qb, mask_override=gmask,
+                                   correction_form=correction_form)
     r1, a1 = rel_l2(got, arith["out"]), float(np.abs(got - arith["out"]).max())
     assert r1 <= rel_tol and a1 <= abs_tol, f"{label}: arithmetic rel-L2 {r1:.3e}, max-abs {a1:.3e}"
     res = {"rel_l2_arith": r1, "max_abs_arith": a1, "flips": n_flip,

@@ -85,7 +85,8 @@ def test_layout_offsets(lib):
     from free_block_sparse_mean_amd import binding
     lay = binding.sol_workspace_layout()
     assert lib.sol_attn_workspace_layout(2, 3, 64 * 100, 128, ctypes.byref(lay)) == 0
-    offs = [lay.kbar_t, lay.kbar, lay.vsum, lay.kmean, lay.kcov, lay.vt, lay.qbar, lay.scratch]
+    offs = [lay.kbar_t, lay.kbar, lay.vsum, lay.kmean, lay.kcov, lay.vt, lay.qbar, lay.kbar_bf,
+            lay.vbar_t, lay.scratch]
     assert offs == sorted(offs) and offs[0] == 0 and lay.total_bytes > lay.scratch
     assert all(o % 256 == 0 for o in offs)
     assert lay.kbar - lay.kbar_t >= 6 * 128 * 100 * 4

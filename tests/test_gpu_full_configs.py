@@ -94,7 +94,8 @@ def test_full_size_sampled(name, beta, correction, gpu_lib):
 
 def test_c5_error_against_dense(gpu_lib):
     """Config 5 report: error of the sparse output against dense attention, per
-    beta and correction setting, on sampled rows of sampled heads (printed)."""
+    beta and correction setting (per-row correction logit, block-level logit,
+    none), on sampled rows of sampled heads (printed)."""
     name = "c5_batched_skewed_64k"
     w, q, k, v, qd, kd, vd = _inputs(name)
     heads = [(0, 0), (1, 23)]
@@ -105,17 +106,18 @@ def test_c5_error_against_dense(gpu_lib):
         qs = np.concatenate([q[b, h, i * 64:(i + 1) * 64].float().numpy() for i in rows[(b, h)]])
         dense[(b, h)] = _dense_rows(qs, k[b, h].float().numpy(), v[b, h].float().numpy())
     lines = []
+    flag_of = {"row": gpu_lib.SOL_CORRECTION_ROW, True: gpu_lib.SOL_CORRECTION, False: 0}
     for beta in w.betas:
         errs = {}
-        for corr in (True, False):
-            out, kept, mask, tau = _run_like_bench(gpu_lib, qd, kd, vd, beta,
-                                                   gpu_lib.SOL_CORRECTION if corr else 0)
+        for corr in ("row", True, False):
+            out, kept, mask, tau = _run_like_bench(gpu_lib, qd, kd, vd, beta, flag_of[corr])
             got = np.concatenate([np.concatenate([out[b, h, i * 64:(i + 1) * 64].float().cpu().numpy()
                                                   for i in rows[(b, h)]]) for (b, h) in heads])
             ref = np.concatenate([dense[bh] for bh in heads])
             errs[corr] = (pu.rel_l2(got, ref), float(np.abs(got - ref).max()),
                           float(mask.float().mean()))
         lines.append(f"beta={beta:+.1f} density={errs[True][2]:.4f} "
+                     f"row corr: rel-L2 {errs['row'][0]:.3e} max-abs {errs['row'][1]:.3e} | "
                      f"corr: rel-L2 {errs[True][0]:.3e} max-abs {errs[True][1]:.3e} | "
                      f"no corr: rel-L2 {errs[False][0]:.3e} max-abs {errs[False][1]:.3e}")
         print(lines[-1], flush=True)

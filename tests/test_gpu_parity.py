@@ -248,3 +248,39 @@ def test_masked_equals_fused_without_correction(gpu_lib):
     gpu_lib.sol_attn_masked(q, k, v, b, words, 0, ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("beta", [0.5, 2.0, math.inf])
+def test_row_correction_parity(w, beta, gpu_lib):
+    """SOL_CORRECTION_ROW against the oracle's per-row correction form (same mask)."""
+    print(f"case row-correction {w.name} beta={beta}", flush=True)
+    q, k, v = wl.make_qkv(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    r = pu.run_gpu(qd, kd, vd, beta, gpu_lib.SOL_CORRECTION_ROW, gpu_lib)
+    assert torch.isfinite(r["out"]).all()
+    for b in range(w.B):
+        for h in range(w.H):
+            pu.check_head(q[b, h], k[b, h], v[b, h], r["out"][b, h].numpy(), r["mask"][b, h].numpy(),
+                          r["tau"][b, h].numpy(), beta, True, w.dtype,
+                          label=f"{w.name} b{b} h{h} beta={beta} row", correction_form="row")
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_row_correction_exact_for_constant_key_blocks(dtype, gpu_lib):
+    """Constant key blocks: the per-row correction reproduces dense attention at any beta."""
+    rng = np.random.default_rng(11)
+    nb, d = 70, 64
+    q = rng.standard_normal((1, 1, nb * 64, d)).astype(np.float32)
+    k = np.repeat(rng.standard_normal((1, 1, nb, d)).astype(np.float32), 64, axis=2)
+    v = rng.standard_normal((1, 1, nb * 64, d)).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == BF else torch.float32
+    qt, kt, vt = (torch.from_numpy(x).to(tdt) for x in (q, k, v))
+    from oracle import sol_oracle as orc
+    dense = orc.dense_attention(qt[0, 0].float().numpy(), kt[0, 0].float().numpy(), vt[0, 0].float().numpy())
+    for beta in (0.0, 1.5):
+        r = pu.run_gpu(qt.cuda(), kt.cuda(), vt.cuda(), beta, gpu_lib.SOL_CORRECTION_ROW, gpu_lib)
+        got = r["out"][0, 0].numpy()
+        rel, mab = (pu.BF16_REL_L2, pu.BF16_MAX_ABS) if dtype == BF else (pu.F32_REL_L2, pu.F32_MAX_ABS)
+        assert 0 < r["mask"].sum() < nb * nb
+        assert pu.rel_l2(got, dense) <= rel and float(np.abs(got - dense).max()) <= mab

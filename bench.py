@@ -326,16 +326,16 @@ def main() -> int:
         }
 
     head = measure(args.beta, corr, args.steps, args.warmup)
-    rows = row_stats(kept)
-    balance = load_balance(sb, qd, kd, vd, out, ws, args.beta, corr, w)
-    ablation = routing_overhead(sb, qd, kd, vd, out, ws, args.beta, w, max(3, args.steps // 2))
-    rowc = None if args.no_correction else measure(args.beta, sb.SOL_CORRECTION_ROW, max(3, args.steps // 2), 1)
-    study = None if args.no_routing_study else routing_study(sb, qd, kd, vd, out, ws, w, 5)
     # the two-call step equals one sol_attn_fwd_ex call (bit for bit)
     ref = out.clone()
     sb.sol_attn_fwd_ex(qd, kd, vd, out, args.beta, corr, workspace=ws)
     torch.cuda.synchronize()
     same_as_fwd_ex = bool(torch.equal(ref, out))
+    rows = row_stats(kept)
+    balance = load_balance(sb, qd, kd, vd, out, ws, args.beta, corr, w)
+    ablation = routing_overhead(sb, qd, kd, vd, out, ws, args.beta, w, max(3, args.steps // 2))
+    rowc = None if args.no_correction else measure(args.beta, sb.SOL_CORRECTION_ROW, max(3, args.steps // 2), 1)
+    study = None if args.no_routing_study else routing_study(sb, qd, kd, vd, out, ws, w, 5)
 
     per_beta = {str(args.beta): head}
     small_steps = max(3, args.steps // 2)

@@ -231,7 +231,8 @@ def sol_attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: float,
                        query_blocks: Optional[Sequence[int]] = None,
                        mask_override: Optional[np.ndarray] = None,
                        route_dtype=np.float32,
-                       correction_form: str = "block") -> Dict[str, np.ndarray]:
+                       correction_form: str = "block",
+                       text_blocks: int = 0) -> Dict[str, np.ndarray]:
     """Sol-Attn forward for one head. q, k, v: [N, d] (any float dtype; upcast to float64).
 
     Returns a dict with
@@ -244,6 +245,11 @@ def sol_attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: float,
     can be compared separately from the selection.
     correction_form: "block" (the logit of a block's virtual tokens is s_hat_ij)
     or "row" (q_r . k_bar_j / sqrt(d) for row r, see _attend_query_block).
+    text_blocks: joint attention with a text segment of that many blocks at the
+    end of the sequence, always computed exactly ([IT] "Dove leggere con
+    attenzione": text tokens in joint attention are always exact). Reading: the
+    selection runs as usual over all n_b key blocks, then every query block
+    keeps the text key blocks and a text query block keeps every key block.
     """
     if correction_form not in ("block", "row"):
         raise ValueError("correction_form must be 'block' or 'row'")
@@ -261,6 +267,10 @@ def sol_attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: float,
     mu, sigma = row_mean_std(s_hat)
     tau = thresholds(mu, sigma, beta)
     mask = select_blocks(s_hat, tau)
+    if text_blocks:
+        t0 = nb - int(text_blocks)
+        mask[:, t0:] = True
+        mask[qb >= t0, :] = True
     use = mask if mask_override is None else np.asarray(mask_override, dtype=bool)
 
     kbar_rows = block_means(k64) if correction_form == "row" else None

@@ -466,3 +466,21 @@ def test_row_correction_only_is_attention_over_summaries():
     np.testing.assert_allclose(r["out"], orc.dense_attention(q, kb, vb), rtol=1e-11, atol=1e-12)
     with pytest.raises(ValueError):
         orc.sol_attention_head(q, k, v, 1.0, True, correction_form="tokens")
+
+
+# ---- joint attention with an exact text segment ------------------------------
+
+def test_text_segment_rows_and_columns_exact():
+    """Text key blocks are kept by every query block, text query rows equal dense attention,
+    and a text segment covering the whole sequence gives dense attention."""
+    rng = _rng(80)
+    nb, d, T = 12, 8, 3
+    q, k, v = (rng.standard_normal((nb * BLK, d)) for _ in range(3))
+    r = orc.sol_attention_head(q, k, v, 1.5, True, route_dtype=np.float64, text_blocks=T)
+    assert r["mask"][:, nb - T:].all() and r["mask"][nb - T:, :].all()
+    plain = orc.sol_attention_head(q, k, v, 1.5, True, route_dtype=np.float64)
+    assert (r["mask"] >= plain["mask"]).all()
+    dense = orc.dense_attention(q, k, v)
+    np.testing.assert_allclose(r["out"][(nb - T) * BLK:], dense[(nb - T) * BLK:], rtol=1e-11, atol=1e-12)
+    full = orc.sol_attention_head(q, k, v, 2.5, False, route_dtype=np.float64, text_blocks=nb)
+    np.testing.assert_allclose(full["out"], dense, rtol=1e-11, atol=1e-12)

@@ -82,6 +82,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sol_attn_fused.argtypes = [vp, vp, vp, vp, i, i, i, i, f, u, vp, sz,
                                    ctypes.POINTER(sol_debug), vp]
     lib.sol_attn_fused.restype = i
+    lib.sol_attn_fused_joint.argtypes = [vp, vp, vp, vp, i, i, i, i, f, u, i, vp, sz,
+                                         ctypes.POINTER(sol_debug), vp]
+    lib.sol_attn_fused_joint.restype = i
     lib.sol_route.argtypes = [vp, i, i, i, i, u, i, f, i, f, vp, sz, vp, vp, vp, vp, vp]
     lib.sol_route.restype = i
     lib.sol_attn_masked.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, u, vp, sz, vp, vp]
@@ -188,10 +191,17 @@ def sol_block_summaries(k: torch.Tensor, v: torch.Tensor, workspace: torch.Tenso
 
 
 def sol_attn_fused(q, k, v, out, beta: float, flags: int, workspace: torch.Tensor, *,
-                   kept_per_row=None, mask_bits=None, tau=None, item_clock=None, stream=None) -> None:
+                   kept_per_row=None, mask_bits=None, tau=None, item_clock=None, stream=None,
+                   text_blocks: int = 0) -> None:
     _dev(q, k, v, out, workspace)
     B, H, N, d = _shape(q)
     flags |= _dtype_flag(q, k, v, out)
+    if text_blocks:
+        _check(load_library().sol_attn_fused_joint(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d, float(beta), flags,
+            int(text_blocks), workspace.data_ptr(), workspace.numel(),
+            _dbg(kept_per_row, mask_bits, tau, item_clock), _stream(stream)))
+        return
     _check(load_library().sol_attn_fused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                          B, H, N, d, float(beta), flags, workspace.data_ptr(),
                                          workspace.numel(), _dbg(kept_per_row, mask_bits, tau, item_clock),

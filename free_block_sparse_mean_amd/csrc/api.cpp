@@ -124,7 +124,7 @@ sol_status summaries_checked(const sol::Shape& s, const void* k, const void* v, 
 
 sol_status fused_checked(const sol::Shape& s, const void* q, const void* k, const void* v, void* out,
                          float beta, unsigned flags, const void* ws, const sol_debug* dbg,
-                         hipStream_t st) {
+                         hipStream_t st, int text_blocks = 0) {
   sol::FusedArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.ws = sol::bind_workspace(s, const_cast<void*>(ws));
@@ -139,6 +139,7 @@ sol_status fused_checked(const sol::Shape& s, const void* q, const void* k, cons
   a.tau = dbg ? dbg->tau : nullptr;
   a.item_clock = dbg ? dbg->item_clock : nullptr;
   a.mask_in = nullptr;
+  a.text_blocks = text_blocks;
   hipError_t e = sol::launch_fused(s, dtype_of(flags), a, st);
   if (e != hipSuccess) return device_fail(e, "fused kernel launch");
   return SOL_OK;
@@ -256,6 +257,7 @@ sol_status sol_attn_masked(const void* q, const void* k, const void* v, void* ou
   a.tau = nullptr;
   a.item_clock = nullptr;
   a.mask_in = mask_bits;
+  a.text_blocks = 0;
   hipError_t e = sol::launch_fused(s, dtype_of(flags), a, str);
   if (e != hipSuccess) return device_fail(e, "given-mask kernel launch");
   return finish(flags, str);
@@ -296,6 +298,24 @@ sol_status sol_route(const void* q, int B, int H, int N, int d, unsigned flags, 
   a.idx = mode == SOL_ROUTE_TOPK ? topk_idx : nullptr;
   hipError_t e = sol::launch_route(s, dtype_of(flags), a, str);
   if (e != hipSuccess) return device_fail(e, "routing launch");
+  return finish(flags, str);
+}
+
+sol_status sol_attn_fused_joint(const void* q, const void* k, const void* v, void* out, int B,
+                                int H, int N, int d, float beta, unsigned flags, int text_blocks,
+                                const void* workspace, size_t ws_bytes, const sol_debug* dbg,
+                                void* hip_stream) {
+  sol::Shape s;
+  sol_status st = check_shape(B, H, N, d, &s);
+  if (st != SOL_OK) return st;
+  if ((st = check_fused_args(q, k, v, out, beta, flags)) != SOL_OK) return st;
+  if (text_blocks < 0 || text_blocks > s.n_b)
+    return fail(SOL_ERR_INVALID_ARG, "text_blocks must be in [0, n_b] (got %d, n_b %d)", text_blocks, s.n_b);
+  if (!workspace || ws_bytes < sol::make_layout(s).total)
+    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
+                ws_bytes, workspace ? "" : ", NULL");
+  hipStream_t str = static_cast<hipStream_t>(hip_stream);
+  if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str, text_blocks)) != SOL_OK) return st;
   return finish(flags, str);
 }
 

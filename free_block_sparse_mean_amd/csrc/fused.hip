@@ -78,6 +78,7 @@ struct FusedParams {
   float* tau_out;
   uint64_t* item_clock;
   const uint64_t* mask_in;   // caller-given selection (kModeGiven), [BH][n_b][n_words]
+  int text_blocks;           // the last text_blocks blocks are text: always kept, dense rows
 };
 
 template <typename T, int D> struct Geom;
@@ -660,6 +661,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---- 3b. strict test against tau -> one 64-bit word per 64 key blocks ------
   {
+    const int t0 = n_b - p.text_blocks;
     float cmax[kGMax] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     float kept[kGMax] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -670,7 +672,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const int j = wi * 64 + lane;
           const bool valid = j < n_b;
           const float s = valid ? shr[g][j] : 0.f;
-          const bool keep = valid && (s > tau);
+          // text key blocks and text query blocks (joint attention) are always exact
+          const bool keep = valid && (s > tau || j >= t0 || qi0 + g >= t0);
           const uint64_t word = __ballot(keep);
           if (valid && !keep) cmax[g] = fmaxf(cmax[g], s);
           if (lane == 0) masks[g * n_words + wi] = word;
@@ -936,6 +939,7 @@ hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
   p.kept_per_row = a.kept_per_row; p.mask_bits = a.mask_bits; p.tau_out = a.tau;
   p.item_clock = a.item_clock;
   p.mask_in = a.mask_in;
+  p.text_blocks = a.text_blocks;
   const dim3 grid((unsigned)(8 * g.per_xcd * s.BH()));
   const void* fn = a.mask_in          ? (const void*)fused_kernel<T, D, kModeGiven>
                    : a.correction_row ? (const void*)fused_kernel<T, D, kModeCorrRow>

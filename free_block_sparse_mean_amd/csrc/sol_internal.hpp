@@ -72,6 +72,7 @@ struct FusedArgs {
   float* tau;
   uint64_t* item_clock;
   const uint64_t* mask_in;   // non-null: caller-given selection, no routing and no correction
+  int text_blocks;           // joint attention: the last text_blocks blocks are text (always exact)
 };
 
 // Routing baselines with a materialized proxy map (route.hip).

@@ -155,6 +155,20 @@ sol_status sol_attn_fused(const void* q, const void* k, const void* v, void* out
                           const void* workspace, size_t ws_bytes, const sol_debug* dbg,
                           void* hip_stream);
 
+/* The fused pass for joint attention with a text segment: the last text_blocks
+ * blocks of the sequence are text tokens, which are always computed exactly
+ * (page "Sol-Attn: l'attenzione sparsa che sceglie al volo" (paithon.it),
+ * section "Dove leggere con attenzione": text tokens in joint attention are
+ * always exact). The selection runs as in sol_attn_fused over all n_b key
+ * blocks; then every query block also keeps the text key blocks, and a text
+ * query block keeps every key block (a dense row). The caller pads the text
+ * segment to whole 64-token blocks. text_blocks in [0, n_b], else
+ * SOL_ERR_INVALID_ARG; 0 is sol_attn_fused. Other arguments as sol_attn_fused. */
+sol_status sol_attn_fused_joint(const void* q, const void* k, const void* v, void* out,
+                                int B, int H, int N, int d, float beta, unsigned flags,
+                                int text_blocks, const void* workspace, size_t ws_bytes,
+                                const sol_debug* dbg, void* hip_stream);
+
 /* Block-sparse attention on a caller-given selection: no routing and no
  * correction, the same exact-attention pass as sol_attn_fused on the same
  * blocks. It is the plain block-sparse kernel the fused pass is measured

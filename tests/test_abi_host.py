@@ -117,3 +117,12 @@ def test_route_validation(lib):
     assert lib.sol_route(p, 1, 1, 4096, 64, 0, 2, 0.0, 0, math.nan, p, big, p, p, None, None, None) == 1
     assert lib.sol_route(p, 1, 1, 4096, 64, 0x2, 0, 1.0, 0, 0.0, p, big, p, p, None, None, None) == 1
     assert lib.sol_route(p, 1, 1, 4096, 64, 0, 0, 1.0, 0, 0.0, p, 10, p, p, None, None, None) == 5
+
+
+def test_joint_validation(lib):
+    p = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    big = 1 << 30
+    assert lib.sol_attn_fused_joint(p, p, p, p, 1, 1, 4096, 64, 1.0, 0, -1, p, big, None, None) == 1
+    assert lib.sol_attn_fused_joint(p, p, p, p, 1, 1, 4096, 64, 1.0, 0, 65, p, big, None, None) == 1
+    assert "text_blocks" in lib.sol_last_error().decode()
+    assert lib.sol_attn_fused_joint(p, p, p, p, 1, 1, 4096, 64, 1.0, 0, 3, p, 10, None, None) == 5

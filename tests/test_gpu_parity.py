@@ -284,3 +284,39 @@ def test_row_correction_exact_for_constant_key_blocks(dtype, gpu_lib):
         rel, mab = (pu.BF16_REL_L2, pu.BF16_MAX_ABS) if dtype == BF else (pu.F32_REL_L2, pu.F32_MAX_ABS)
         assert 0 < r["mask"].sum() < nb * nb
         assert pu.rel_l2(got, dense) <= rel and float(np.abs(got - dense).max()) <= mab
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[1], SMALL[5]], ids=lambda w: w.name)
+@pytest.mark.parametrize("flags_name", ["SOL_CORRECTION", "SOL_CORRECTION_ROW", None])
+def test_joint_text_segment(w, flags_name, gpu_lib):
+    """Joint attention: the last T blocks are text, always exact (kept columns, dense rows)."""
+    print(f"case joint {w.name} {flags_name}", flush=True)
+    T = 3
+    q, k, v = wl.make_qkv(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    nb = w.n_blocks
+    W = (nb + 63) // 64
+    flags = getattr(gpu_lib, flags_name) if flags_name else 0
+    ws = gpu_lib.new_workspace(w.B, w.H, w.N, w.d)
+    out = torch.empty_like(qd)
+    mask = torch.zeros((w.B, w.H, nb, W), dtype=torch.int64, device=qd.device)
+    tau = torch.empty((w.B, w.H, nb), dtype=torch.float32, device=qd.device)
+    gpu_lib.sol_block_summaries(kd, vd, ws)
+    gpu_lib.sol_attn_fused(qd, kd, vd, out, 1.5, flags, ws, mask_bits=mask, tau=tau, text_blocks=T)
+    torch.cuda.synchronize()
+    m = gpu_lib.decode_mask(mask, nb).numpy()
+    assert m[..., nb - T:].all() and m[:, :, nb - T:, :].all()
+    got = out.float().cpu().numpy()
+    rel, mab = (pu.BF16_REL_L2, pu.BF16_MAX_ABS) if w.dtype == BF else (pu.F32_REL_L2, pu.F32_MAX_ABS)
+    from oracle import sol_oracle as orc
+    form = "row" if flags_name == "SOL_CORRECTION_ROW" else "block"
+    for b in range(w.B):
+        for h in range(w.H):
+            r = orc.sol_attention_head(q[b, h].float().numpy(), k[b, h].float().numpy(),
+                                       v[b, h].float().numpy(), 1.5, flags != 0, mask_override=m[b, h],
+                                       correction_form=form, text_blocks=T)
+            assert pu.rel_l2(got[b, h], r["out"]) <= rel
+            assert float(np.abs(got[b, h] - r["out"]).max()) <= mab
+            diff = r["mask"] != m[b, h]
+            if diff.any():
+                assert np.abs(r["s_hat"] - r["tau"][:, None])[diff].max() <= pu.TIE_BAND

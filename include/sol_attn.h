@@ -158,8 +158,8 @@ sol_status sol_attn_fused(const void* q, const void* k, const void* v, void* out
 /* The fused pass for joint attention with a text segment: the last text_blocks
  * blocks of the sequence are text tokens, which are always computed exactly
  * (page "Sol-Attn: l'attenzione sparsa che sceglie al volo" (paithon.it),
- * section "Dove leggere con attenzione": text tokens in joint attention are
- * always exact). The selection runs as in sol_attn_fused over all n_b key
+ * section "Dove leggere con attenzione": the evaluated systems compute text
+ * tokens exactly). The selection runs as in sol_attn_fused over all n_b key
  * blocks; then every query block also keeps the text key blocks, and a text
  * query block keeps every key block (a dense row). The caller pads the text
  * segment to whole 64-token blocks. text_blocks in [0, n_b], else

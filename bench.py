@@ -87,6 +87,91 @@ def time_steps(fn_pre, fn_fused, steps: int):
     return ms, sum(fused_each) / steps, pre, wall, fused_each
 
 
+def time_flushed(fn_pre, fn_fused, reps: int, flush=None):
+    """Time `reps` steps one at a time, each after `flush` (if given) has evicted the
+    inputs from the Infinity Cache; returns (median step ms, median fused ms, median
+    pre-pass ms, fused ms of each step)."""
+    import torch
+    st = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    steps, fused, pre = [], [], []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a, b, c = ev(), ev(), ev()
+        a.record(st)
+        fn_pre()
+        b.record(st)
+        fn_fused()
+        c.record(st)
+        torch.cuda.synchronize()
+        steps.append(a.elapsed_time(c))
+        pre.append(a.elapsed_time(b))
+        fused.append(b.elapsed_time(c))
+    return statistics.median(steps), statistics.median(fused), statistics.median(pre), fused
+
+
+SWEEP_BETAS = {"c4_stress_128k": (1.2816, 1.5, 1.645, 2.0)}
+
+
+def sweep(names, reps: int) -> int:
+    """Per-config timing of every beta the configuration lists (with the correction, and
+    without it for the batched skewed config) and of the dense path: one JSON line per
+    configuration. Inputs smaller than twice the Infinity Cache are flushed before each
+    step by writing a 512 MiB buffer."""
+    import torch
+    from free_block_sparse_mean_amd import binding as sb, workloads as wl
+    dev = torch.device("cuda:0")
+    for name in names:
+        w = wl.CONFIGS[name]
+        q, k, v = wl.make_qkv(w)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        del q, k, v
+        out = torch.empty_like(qd)
+        ws = sb.new_workspace(w.B, w.H, w.N, w.d, dev)
+        nb = w.n_blocks
+        kept = torch.zeros((w.B, w.H, nb), dtype=torch.int32, device=dev)
+        in_bytes = 3 * qd.numel() * qd.element_size()
+        flush = None
+        if in_bytes < 2 * 256 * 2 ** 20:
+            junk = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+            flush = lambda: junk.fill_(1)
+        pre = lambda: sb.sol_block_summaries(kd, vd, ws)
+
+        def one(beta, flags):
+            sb.sol_block_summaries(kd, vd, ws)
+            sb.sol_attn_fused(qd, kd, vd, out, beta, flags, ws, kept_per_row=kept)
+            torch.cuda.synchronize()
+            n_kept = int(kept.sum().item())
+            fused = lambda: sb.sol_attn_fused(qd, kd, vd, out, beta, flags, ws)
+            pre(); fused()
+            ms, fms, pms, each = time_flushed(pre, fused, reps, flush)
+            kf = kept_flop(w, n_kept)
+            return {"beta": beta if math.isfinite(beta) else str(beta),
+                    "correction": bool(flags & sb.SOL_CORRECTION), "ms": ms, "fused_ms": fms,
+                    "prepass_ms": pms, "fused_ms_min": min(each),
+                    "density": n_kept / (w.B * w.H * nb * nb),
+                    "dense_equiv_tflops": dense_equiv_flop(w) / (ms * 1e-3) / 1e12,
+                    "kept_tflops_fused": kf / (fms * 1e-3) / 1e12,
+                    "mfma_frac_fused": kf / (fms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+        rows = []
+        betas = SWEEP_BETAS.get(name, w.betas)
+        corr_opts = (sb.SOL_CORRECTION, 0) if w.skewed else (sb.SOL_CORRECTION,)
+        for beta in betas:
+            for c in corr_opts:
+                rows.append(one(beta, c))
+        dense = one(-math.inf, sb.SOL_CORRECTION | sb.SOL_DENSE)
+        for r in rows:
+            r["speedup_vs_dense"] = dense["ms"] / r["ms"]
+        print(json.dumps({"sweep": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                          "flushed": flush is not None, "reps": reps, "settings": rows,
+                          "dense": dense}), flush=True)
+        del qd, kd, vd, out, ws, kept
+        torch.cuda.empty_cache()
+    return 0
+
+
 def cpu_baseline(w, q, k, v, beta: float, blocks_per_head: int, heads):
     """The oracle, untuned, on a bounded sample: `blocks_per_head` seeded query blocks of
     each listed head. Returns the dense-equivalent TFLOP/s of the sampled rows."""
@@ -260,6 +345,9 @@ def main() -> int:
     ap.add_argument("--cpu-blocks-per-head", type=int, default=128)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (for counter scaling)")
+    ap.add_argument("--sweep", default="",
+                    help="comma list of bf16 configs to time at every beta they list (one JSON "
+                         "line each) instead of the headline benchmark")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -271,6 +359,9 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 2
+
+    if args.sweep:
+        return sweep([x for x in args.sweep.split(",") if x], max(3, args.steps // 2))
 
     if args.copy_calibration:
         n = 512 * 2 ** 20

@@ -51,6 +51,10 @@ class sol_debug(ctypes.Structure):
                 ("item_clock", ctypes.c_void_p)]
 
 
+class sol_strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
 class sol_workspace_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("total_bytes", "kbar_t", "kbar", "vsum", "kmean", "kcov", "vt", "qbar", "kbar_bf",
@@ -94,6 +98,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sol_attn_fwd_ex.restype = i
     lib.sol_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, f, u]
     lib.sol_attn_fwd.restype = i
+    sp = ctypes.POINTER(sol_strides)
+    lib.sol_attn_fwd_strided.argtypes = [vp, vp, vp, vp, i, i, i, i, sp, sp, sp, sp, f, u, vp, vp, sz,
+                                         ctypes.POINTER(sol_debug)]
+    lib.sol_attn_fwd_strided.restype = i
     _lib = lib
     return lib
 
@@ -255,6 +263,32 @@ def sol_attn_fwd_ex(q, k, v, out, beta: float, flags: int, stream=None,
                                           B, H, N, d, float(beta), flags, _stream(stream),
                                           workspace.data_ptr(), workspace.numel(),
                                           _dbg(kept_per_row, mask_bits, tau, item_clock)))
+
+
+def _strides(t: torch.Tensor):
+    """sol_strides of a logical [B, H, N, d] view whose last dimension is contiguous."""
+    if not t.is_cuda or t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("tensors must be [B, H, N, d] device views with contiguous rows of d")
+    return ctypes.byref(sol_strides(t.stride(0), t.stride(1), t.stride(2)))
+
+
+def sol_attn_fwd_strided(q, k, v, out, beta: float, flags: int, stream=None,
+                         workspace: Optional[torch.Tensor] = None, *, kept_per_row=None,
+                         mask_bits=None, tau=None, item_clock=None) -> None:
+    """sol_attn_fwd_ex on [B, H, N, d] views of any strides (rows of d contiguous), e.g.
+    x.transpose(1, 2) of a [B, N, H, d] tensor or slices of a packed QKV projection."""
+    B, H, N, d = _shape(q)
+    for t in (k, v, out):
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError("q, k, v and out must have the same [B, H, N, d] shape")
+    sq, sk, sv, so = _strides(q), _strides(k), _strides(v), _strides(out)
+    flags |= _dtype_flag(q, k, v, out)
+    if workspace is None:
+        workspace = new_workspace(B, H, N, d, q.device)
+    _check(load_library().sol_attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                               B, H, N, d, sq, sk, sv, so, float(beta), flags,
+                                               _stream(stream), workspace.data_ptr(), workspace.numel(),
+                                               _dbg(kept_per_row, mask_bits, tau, item_clock)))
 
 
 def sol_attn_fwd(q, k, v, out, beta: float, flags: int) -> None:

@@ -115,16 +115,17 @@ sol_status finish(unsigned flags, hipStream_t st) {
 }
 
 sol_status summaries_checked(const sol::Shape& s, const void* k, const void* v, unsigned flags,
-                             void* ws, hipStream_t st) {
+                             void* ws, hipStream_t st, const sol::IoStrides* io = nullptr) {
   const sol::Workspace w = sol::bind_workspace(s, ws);
-  hipError_t e = sol::launch_prepass(s, dtype_of(flags), k, v, w, st);
+  const sol::IoStrides x = io ? *io : sol::contiguous_io(s);
+  hipError_t e = sol::launch_prepass(s, dtype_of(flags), k, v, x.k, x.v, w, st);
   if (e != hipSuccess) return device_fail(e, "block-summary pre-pass launch");
   return SOL_OK;
 }
 
 sol_status fused_checked(const sol::Shape& s, const void* q, const void* k, const void* v, void* out,
                          float beta, unsigned flags, const void* ws, const sol_debug* dbg,
-                         hipStream_t st, int text_blocks = 0) {
+                         hipStream_t st, int text_blocks = 0, const sol::IoStrides* io = nullptr) {
   sol::FusedArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.ws = sol::bind_workspace(s, const_cast<void*>(ws));
@@ -140,6 +141,7 @@ sol_status fused_checked(const sol::Shape& s, const void* q, const void* k, cons
   a.item_clock = dbg ? dbg->item_clock : nullptr;
   a.mask_in = nullptr;
   a.text_blocks = text_blocks;
+  a.io = io ? *io : sol::contiguous_io(s);
   hipError_t e = sol::launch_fused(s, dtype_of(flags), a, st);
   if (e != hipSuccess) return device_fail(e, "fused kernel launch");
   return SOL_OK;
@@ -150,6 +152,32 @@ sol_status check_fused_args(const void* q, const void* k, const void* v, void* o
   if (!q || !k || !v || !out) return fail(SOL_ERR_INVALID_ARG, "q, k, v and out must be non-null");
   if (isnan(beta)) return fail(SOL_ERR_INVALID_ARG, "beta is NaN");
   return check_flags(flags);
+}
+
+// Strides of one tensor from the caller (NULL: contiguous), validated.
+sol_status take_strides(const sol::Shape& s, unsigned flags, const sol_strides* in, const void* ptr,
+                        const char* name, bool is_out, sol::TStrides* st) {
+  if (reinterpret_cast<uintptr_t>(ptr) % 16)
+    return fail(SOL_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  if (!in) {
+    *st = sol::contiguous_strides(s);
+    return SOL_OK;
+  }
+  const long long unit = (flags & SOL_F32) ? 4 : 8;   // elements per 16 bytes
+  const long long v[3] = {in->b, in->h, in->n};
+  const int ext[3] = {s.B, s.H, s.N};
+  const char* dim[3] = {"b", "h", "n"};
+  for (int i = 0; i < 3; ++i) {
+    if (v[i] < 0 || (v[i] == 0 && ext[i] > 1))
+      return fail(SOL_ERR_INVALID_ARG, "%s stride %s must be positive (got %lld)", name, dim[i], v[i]);
+    if (v[i] % unit)
+      return fail(SOL_ERR_INVALID_ARG, "%s stride %s must be a multiple of %lld elements (got %lld)", name,
+                  dim[i], unit, v[i]);
+  }
+  if (in->n >= (1ll << 24)) return fail(SOL_ERR_INVALID_ARG, "%s stride n must be below 2^24", name);
+  if (is_out && in->n < s.d) return fail(SOL_ERR_INVALID_ARG, "%s stride n must be at least d", name);
+  *st = sol::TStrides{in->b, in->h, in->n};
+  return SOL_OK;
 }
 
 // Library-owned workspace of sol_attn_fwd, one per device.
@@ -258,6 +286,7 @@ sol_status sol_attn_masked(const void* q, const void* k, const void* v, void* ou
   a.item_clock = nullptr;
   a.mask_in = mask_bits;
   a.text_blocks = 0;
+  a.io = sol::contiguous_io(s);
   hipError_t e = sol::launch_fused(s, dtype_of(flags), a, str);
   if (e != hipSuccess) return device_fail(e, "given-mask kernel launch");
   return finish(flags, str);
@@ -286,6 +315,7 @@ sol_status sol_route(const void* q, int B, int H, int N, int d, unsigned flags, 
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   sol::RouteArgs a;
   a.q = q;
+  a.qs = sol::contiguous_strides(s);
   a.ws = sol::bind_workspace(s, const_cast<void*>(workspace));
   a.mode = mode;
   a.beta = beta;
@@ -332,6 +362,29 @@ sol_status sol_attn_fwd_ex(const void* q, const void* k, const void* v, void* ou
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   if ((st = summaries_checked(s, k, v, flags, workspace, str)) != SOL_OK) return st;
   if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str)) != SOL_OK) return st;
+  return finish(flags, str);
+}
+
+sol_status sol_attn_fwd_strided(const void* q, const void* k, const void* v, void* out, int B, int H,
+                                int N, int d, const sol_strides* q_strides, const sol_strides* k_strides,
+                                const sol_strides* v_strides, const sol_strides* out_strides, float beta,
+                                unsigned flags, void* hip_stream, void* workspace, size_t ws_bytes,
+                                const sol_debug* dbg) {
+  sol::Shape s;
+  sol_status st = check_shape(B, H, N, d, &s);
+  if (st != SOL_OK) return st;
+  if ((st = check_fused_args(q, k, v, out, beta, flags)) != SOL_OK) return st;
+  sol::IoStrides io;
+  if ((st = take_strides(s, flags, q_strides, q, "q", false, &io.q)) != SOL_OK) return st;
+  if ((st = take_strides(s, flags, k_strides, k, "k", false, &io.k)) != SOL_OK) return st;
+  if ((st = take_strides(s, flags, v_strides, v, "v", false, &io.v)) != SOL_OK) return st;
+  if ((st = take_strides(s, flags, out_strides, out, "out", true, &io.o)) != SOL_OK) return st;
+  if (!workspace || ws_bytes < sol::make_layout(s).total)
+    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
+                ws_bytes, workspace ? "" : ", NULL");
+  hipStream_t str = static_cast<hipStream_t>(hip_stream);
+  if ((st = summaries_checked(s, k, v, flags, workspace, str, &io)) != SOL_OK) return st;
+  if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str, 0, &io)) != SOL_OK) return st;
   return finish(flags, str);
 }
 

@@ -71,6 +71,8 @@ struct FusedParams {
   int n_b, n_b_pad, n_words, G, n_groups;
   long long BH, per_xcd;   // per_xcd: work items of one head given to each XCD
   long long N;
+  int H;
+  TStrides qs, ks, vs, os;   // element strides of q, k, v and out (rows of d are contiguous)
   float beta;
   int beta_mode;
   int32_t* kept_per_row;
@@ -223,20 +225,27 @@ typedef __attribute__((address_space(1))) const void gbl_ptr_t;
 // slabs), slabs are 4096 bytes apart in both global memory and LDS, and the
 // LDS destination of a wave is uniform (kept in a scalar register).
 struct DmaLane {
-  int k_off;      // byte offset of this lane's K chunk in slab 0 of the tile
-  int v_off;      // byte offset of this lane's V^T chunk in slab 0
-  int wave_lds;   // this wave's first LDS byte inside a slab (uniform)
+  int k_off;         // byte offset of this lane's K chunk in slab 0 of a tile of the input K
+  long long k_slab;  // bytes between slabs of the input K (16 or 32 rows; uniform)
+  int kc_off;        // the same offset in a contiguous [64][D] tile (block summaries)
+  int v_off;         // byte offset of this lane's V^T chunk in slab 0
+  int wave_lds;      // this wave's first LDS byte inside a slab (uniform)
 };
+// k_row: row stride of the input K in elements
 template <int D>
-__device__ __forceinline__ DmaLane dma_lane(int t) {
+__device__ __forceinline__ DmaLane dma_lane(int t, long long k_row) {
   DmaLane dl;
+  constexpr int RPS = 4096 / (D * 2);   // rows per 4096-byte slab
   if constexpr (D == 128) {
     const int r = t >> 4, c = (t & 15) ^ (r & 15);          // rows of 16 chunks
-    dl.k_off = r * D * 2 + c * 16;
+    dl.k_off = (int)(r * k_row * 2) + c * 16;
+    dl.kc_off = r * D * 2 + c * 16;
   } else {
     const int r = t >> 3, c = (t & 7) ^ ((r >> 1) & 7);     // rows of 8 chunks
-    dl.k_off = r * D * 2 + c * 16;
+    dl.k_off = (int)(r * k_row * 2) + c * 16;
+    dl.kc_off = r * D * 2 + c * 16;
   }
+  dl.k_slab = RPS * k_row * 2;
   const int d = t >> 3, kc = (t & 7) ^ ((d >> 1) & 7);      // V^T rows of 8 chunks
   dl.v_off = d * 128 + kc * 16;
   dl.wave_lds = __builtin_amdgcn_readfirstlane((t >> 6) * 1024);
@@ -244,17 +253,20 @@ __device__ __forceinline__ DmaLane dma_lane(int t) {
 }
 
 // bf16: start loading the K tile and the transposed V tile of key block j
-// straight into LDS buffer `buf`. Completion is awaited with s_waitcnt vmcnt
+// straight into LDS buffer `buf`. The K source is either the input K (row
+// stride from the caller) or a contiguous tile of block summaries: k_off is
+// this lane's byte offset in the first slab of 4096 / (2 D) rows and k_slab
+// the byte distance between slabs. Completion is awaited with s_waitcnt vmcnt
 // before the next barrier.
 template <int D>
-__device__ __forceinline__ void issue_tile(unsigned char* buf, const __bf16* Ksrc, const __bf16* Vsrc,
-                                           const DmaLane& dl) {
+__device__ __forceinline__ void issue_tile(unsigned char* buf, const __bf16* Ksrc, int k_off, long long k_slab,
+                                           const __bf16* Vsrc, const DmaLane& dl) {
   constexpr int NI = D / 32;   // slabs per region
-  const unsigned char* Kj = reinterpret_cast<const unsigned char*>(Ksrc);   // [64][D]
+  const unsigned char* Kj = reinterpret_cast<const unsigned char*>(Ksrc);   // 64 rows of D
   const unsigned char* Vj = reinterpret_cast<const unsigned char*>(Vsrc);   // [D][64]
 #pragma unroll
   for (int i = 0; i < NI; ++i)
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(Kj + dl.k_off + i * 4096),
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(Kj + k_off + i * k_slab),
                                      (lds_ptr_t*)(buf + i * 4096 + dl.wave_lds), 16, 0, 0);
 #pragma unroll
   for (int i = 0; i < NI; ++i)
@@ -266,17 +278,17 @@ __device__ __forceinline__ void issue_tile(unsigned char* buf, const __bf16* Ksr
 // fp32: stage the K and V tiles of key block j in LDS (synchronously)
 template <int D>
 __device__ __forceinline__ void commit_f32(float* stK, float* stV, const float* Kh, const float* Vh,
-                                           int j, int t) {
+                                           long long k_row, long long v_row, int j, int t) {
   using Gm = Geom<float, D>;
-  const float* Kj = Kh + (size_t)j * kBlock * D;
-  const float* Vj = Vh + (size_t)j * kBlock * D;
+  const float* Kj = Kh + (long long)j * kBlock * k_row;
+  const float* Vj = Vh + (long long)j * kBlock * v_row;
   constexpr int CH = D / 4;
   for (int c = t; c < 64 * CH; c += 256) {
     const int r = c / CH, cc = c % CH;
     *reinterpret_cast<float4*>(stK + r * Gm::kKPitch + cc * 4) =
-        reinterpret_cast<const float4*>(Kj + (size_t)r * D)[cc];
+        reinterpret_cast<const float4*>(Kj + (long long)r * k_row)[cc];
     *reinterpret_cast<float4*>(stV + r * Gm::kVPitch + cc * 4) =
-        reinterpret_cast<const float4*>(Vj + (size_t)r * D)[cc];
+        reinterpret_cast<const float4*>(Vj + (long long)r * v_row)[cc];
   }
 }
 
@@ -454,7 +466,8 @@ __device__ __forceinline__ void epilogue(ExactState<T, D>& st, const FusedParams
   const float fc = (c2 == -INFINITY) ? 0.f : fast_exp2(c2 - M);
   const float den = l * fo + Lg * fc;
   const float inv = den > 0.f ? 1.0f / den : 0.f;
-  T* orow = static_cast<T*>(p.out) + ((size_t)bh * p.N + (size_t)qb * kBlock + row) * D;
+  T* orow = static_cast<T*>(p.out) + (bh / p.H) * p.os.b + (bh % p.H) * p.os.h +
+            ((long long)qb * kBlock + row) * p.os.n;
   if constexpr (S::kBF) {
 #pragma unroll
     for (int dt = 0; dt < S::NACC; ++dt) {
@@ -535,9 +548,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                        : reinterpret_cast<float*>(sbufB) + (g - rpb) * nbp;
   }
 
-  const T* Qh = static_cast<const T*>(p.q) + (size_t)bh * p.N * D;
-  const T* Kh = static_cast<const T*>(p.k) + (size_t)bh * p.N * D;
-  const T* Vh = static_cast<const T*>(p.v) + (size_t)bh * p.N * D;
+  const long long ib = bh / p.H, ih = bh % p.H;
+  const T* Qh = static_cast<const T*>(p.q) + ib * p.qs.b + ih * p.qs.h;   // row t at Qh + t * qs.n
+  const T* Kh = static_cast<const T*>(p.k) + ib * p.ks.b + ih * p.ks.h;
+  const T* Vh = static_cast<const T*>(p.v) + ib * p.vs.b + ih * p.vs.h;
 
   if constexpr (MODE == kModeGiven) {
     // ---- caller-given selection: the G blocks' mask words into LDS ----------
@@ -564,14 +578,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int E = V16::kN, CH = D / E, RPT = 64 * CH / 256, RSTEP = 256 / CH;
     const int cc = t % CH, r0 = t / CH;
     for (int g = 0; g < nG; ++g) {
-      const T* Qb = Qh + (size_t)(qi0 + g) * kBlock * D;
+      const T* Qb = Qh + (long long)(qi0 + g) * kBlock * p.qs.n;
       float s[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) s[e] = 0.f;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         float f[E];
-        V16::to_float(reinterpret_cast<const typename V16::raw*>(Qb + (size_t)(r0 + RSTEP * i) * D)[cc], f);
+        V16::to_float(reinterpret_cast<const typename V16::raw*>(Qb + (long long)(r0 + RSTEP * i) * p.qs.n)[cc], f);
 #pragma unroll
         for (int e = 0; e < E; ++e) s[e] += f[e];
       }
@@ -772,12 +786,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // so the other buffer is free), start loading the next union tile into
     // it, compute tile j.
     const LaneOfs<D> lofs(lane);
-    const DmaLane dl = dma_lane<D>(t);
+    const DmaLane dl = dma_lane<D>(t, p.ks.n);
     ExactState<T, D> sts[kGMax];
 #pragma unroll
     for (int g = 0; g < kGMax; ++g) {
       zero_state<T, D>(sts[g]);
-      if (g < nG) load_q<T, D>(sts[g], Qh + ((size_t)(qi0 + g) * kBlock + row) * D, lane);
+      if (g < nG) load_q<T, D>(sts[g], Qh + ((long long)(qi0 + g) * kBlock + row) * p.qs.n, lane);
     }
     auto union_next = [&](int j) -> int {   // next key block after j kept by any block
       for (int wi = (j + 1) >> 6; wi < n_words; ++wi) {
@@ -809,13 +823,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       __builtin_amdgcn_s_barrier();                                               \
       asm volatile("" ::: "memory");                                              \
       if (nj >= 0)                                                                \
-        issue_tile<D>(NEXTB, Kh + (size_t)nj * kBlock * D, Vt + (size_t)nj * D * 64, dl); \
+        issue_tile<D>(NEXTB, Kh + (long long)nj * kBlock * p.ks.n, dl.k_off, dl.k_slab, Vt + (size_t)nj * D * 64, dl); \
       _Pragma("unroll") for (int g = 0; g < kGMax; ++g)                           \
         if (keep & (1u << g)) tile_bf16<D>(sts[g], CURB, lofs);                   \
       j = nj;                                                                     \
     }
     int j = union_next(-1);
-    if (j >= 0) issue_tile<D>(sbufA, Kh + (size_t)j * kBlock * D, Vt + (size_t)j * D * 64, dl);
+    if (j >= 0) issue_tile<D>(sbufA, Kh + (long long)j * kBlock * p.ks.n, dl.k_off, dl.k_slab, Vt + (size_t)j * D * 64, dl);
     while (j >= 0) {
       SOL_STEP(sbufA, sbufB)
       if (j < 0) break;
@@ -831,7 +845,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      issue_tile<D>(sbufA, Kbs, Vbs, dl);
+      issue_tile<D>(sbufA, Kbs, dl.kc_off, 4096, Vbs, dl);
 #define SOL_VSTEP(CURB, NEXTB)                                                    \
       {                                                                           \
         const uint64_t pad = (c == n_words - 1 && (n_b & 63)) ? ~0ull << (n_b & 63) : 0ull; \
@@ -840,7 +854,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_s_barrier();                                             \
         asm volatile("" ::: "memory");                                            \
         if (c + 1 < n_words)                                                      \
-          issue_tile<D>(NEXTB, Kbs + (size_t)(c + 1) * 64 * D, Vbs + (size_t)(c + 1) * D * 64, dl); \
+          issue_tile<D>(NEXTB, Kbs + (size_t)(c + 1) * 64 * D, dl.kc_off, 4096, Vbs + (size_t)(c + 1) * D * 64, dl); \
         _Pragma("unroll") for (int g = 0; g < kGMax; ++g) {                       \
           const uint64_t ex = g < nG ? (masks[g * n_words + c] | pad) : ~0ull;    \
           if (ex != ~0ull) tile_bf16<D, true>(sts[g], CURB, lofs, ex);            \
@@ -868,7 +882,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     ExactState<T, D> st;
     for (int g = 0; g < nG; ++g) {
       zero_state<T, D>(st);
-      load_q<T, D>(st, Qh + ((size_t)(qi0 + g) * kBlock + row) * D, lane);
+      load_q<T, D>(st, Qh + ((long long)(qi0 + g) * kBlock + row) * p.qs.n, lane);
       for (int wi = 0; wi < n_words; ++wi) {
         uint64_t word = masks[g * n_words + wi];
         while (word) {
@@ -876,7 +890,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           word &= word - 1;
           __syncthreads();
           commit_f32<D>(reinterpret_cast<float*>(sbufA), reinterpret_cast<float*>(sbufA + Gm::kKBytes),
-                        reinterpret_cast<const float*>(Kh), reinterpret_cast<const float*>(Vh), j, t);
+                        reinterpret_cast<const float*>(Kh), reinterpret_cast<const float*>(Vh), p.ks.n, p.vs.n, j, t);
           __syncthreads();
           tile_f32<D>(st, sbufA, lane);
         }
@@ -935,6 +949,8 @@ hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
   p.n_b = s.n_b; p.n_b_pad = s.n_b_pad; p.n_words = s.n_words;
   p.G = g.G; p.n_groups = g.n_groups; p.BH = s.BH(); p.per_xcd = g.per_xcd;
   p.N = s.N;
+  p.H = s.H;
+  p.qs = a.io.q; p.ks = a.io.k; p.vs = a.io.v; p.os = a.io.o;
   p.beta = a.beta; p.beta_mode = a.beta_mode;
   p.kept_per_row = a.kept_per_row; p.mask_bits = a.mask_bits; p.tau_out = a.tau;
   p.item_clock = a.item_clock;

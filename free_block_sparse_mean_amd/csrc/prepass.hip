@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const T* __restrict__ k
                                                          float* __restrict__ kbar,
                                                          float* __restrict__ vsum,
                                                          __bf16* __restrict__ vt,
-                                                         int n_b, long long N) {
+                                                         int n_b, int H, TStrides ks, TStrides vs) {
   using V = Vec16<T>;
   constexpr int E = V::kN;     // elements per 16-byte chunk
   constexpr int CH = D / E;    // chunks per row
@@ -52,18 +52,18 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const T* __restrict__ k
   const long long bh = blockIdx.y;
   if (j >= n_b) return;   // whole wave leaves; no workgroup barrier below
   const int cc = lane % CH, rg = lane / CH;
-  const size_t base = ((size_t)bh * N + (size_t)j * kBlock) * D;
-  const typename V::raw* pk = reinterpret_cast<const typename V::raw*>(k + base) + cc;
-  const typename V::raw* pv = reinterpret_cast<const typename V::raw*>(v + base) + cc;
+  const long long ib = bh / H, ih = bh % H;
+  const T* kb0 = k + ib * ks.b + ih * ks.h + (long long)j * kBlock * ks.n;   // row 0 of key block j
+  const T* vb0 = v + ib * vs.b + ih * vs.h + (long long)j * kBlock * vs.n;
   float ak[E], av[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) { ak[e] = 0.f; av[e] = 0.f; }
 #pragma unroll 8
   for (int i = 0; i < RPL; ++i) {
     const int r = rg + RG * i;
-    const typename V::raw rv = pv[(size_t)r * CH];
+    const typename V::raw rv = reinterpret_cast<const typename V::raw*>(vb0 + (long long)r * vs.n)[cc];
     float fk[E], fv[E];
-    V::to_float(pk[(size_t)r * CH], fk);
+    V::to_float(reinterpret_cast<const typename V::raw*>(kb0 + (long long)r * ks.n)[cc], fk);
     V::to_float(rv, fv);
 #pragma unroll
     for (int e = 0; e < E; ++e) { ak[e] += fk[e]; av[e] += fv[e]; }
@@ -229,13 +229,13 @@ __global__ __launch_bounds__(256) void virtual_tiles_kernel(const float* __restr
 }
 
 template <typename T, int D>
-hipError_t prepass_impl(const Shape& s, const void* k, const void* v, const Workspace& ws,
-                        hipStream_t st) {
+hipError_t prepass_impl(const Shape& s, const void* k, const void* v, const TStrides& ks, const TStrides& vs,
+                        const Workspace& ws, hipStream_t st) {
   const unsigned bh = (unsigned)s.BH();
   constexpr bool kVT = std::is_same<T, __bf16>::value;
   hipLaunchKernelGGL((block_sums_kernel<T, D, kVT>), dim3((s.n_b + 3) / 4, bh), dim3(256), 0, st,
                      static_cast<const T*>(k), static_cast<const T*>(v), ws.kbar, ws.vsum, ws.vt,
-                     s.n_b, (long long)s.N);
+                     s.n_b, s.H, ks, vs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((moments_partial_kernel<D>), dim3(s.cov_parts, bh), dim3(256), 0, st, ws.kbar,
@@ -253,13 +253,13 @@ hipError_t prepass_impl(const Shape& s, const void* k, const void* v, const Work
 
 }  // namespace
 
-hipError_t launch_prepass(const Shape& s, Dtype dt, const void* k, const void* v,
-                          const Workspace& ws, hipStream_t stream) {
+hipError_t launch_prepass(const Shape& s, Dtype dt, const void* k, const void* v, const TStrides& ks,
+                          const TStrides& vs, const Workspace& ws, hipStream_t stream) {
   if (dt == Dtype::BF16)
-    return s.d == 64 ? prepass_impl<__bf16, 64>(s, k, v, ws, stream)
-                     : prepass_impl<__bf16, 128>(s, k, v, ws, stream);
-  return s.d == 64 ? prepass_impl<float, 64>(s, k, v, ws, stream)
-                   : prepass_impl<float, 128>(s, k, v, ws, stream);
+    return s.d == 64 ? prepass_impl<__bf16, 64>(s, k, v, ks, vs, ws, stream)
+                     : prepass_impl<__bf16, 128>(s, k, v, ks, vs, ws, stream);
+  return s.d == 64 ? prepass_impl<float, 64>(s, k, v, ks, vs, ws, stream)
+                   : prepass_impl<float, 128>(s, k, v, ks, vs, ws, stream);
 }
 
 }  // namespace sol

@@ -26,7 +26,7 @@ namespace {
 // 16-byte chunks, xor-shuffle folds, then / 64).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void qbar_kernel(const T* __restrict__ q, float* __restrict__ qbar,
-                                                   int n_b, long long N) {
+                                                   int n_b, int H, TStrides qs) {
   using V = Vec16<T>;
   constexpr int E = V::kN, CH = D / E, RG = 64 / CH, RPL = 64 / RG;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -34,15 +34,14 @@ __global__ __launch_bounds__(256) void qbar_kernel(const T* __restrict__ q, floa
   const long long bh = blockIdx.y;
   if (i >= n_b) return;   // whole wave leaves; no barrier in this kernel
   const int cc = lane % CH, rg = lane / CH;
-  const typename V::raw* pq =
-      reinterpret_cast<const typename V::raw*>(q + ((size_t)bh * N + (size_t)i * kBlock) * D) + cc;
+  const T* q0 = q + (bh / H) * qs.b + (bh % H) * qs.h + (long long)i * kBlock * qs.n;   // row 0 of block i
   float a[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) a[e] = 0.f;
 #pragma unroll 8
   for (int r = 0; r < RPL; ++r) {
     float f[E];
-    V::to_float(pq[(size_t)(rg + RG * r) * CH], f);
+    V::to_float(reinterpret_cast<const typename V::raw*>(q0 + (long long)(rg + RG * r) * qs.n)[cc], f);
 #pragma unroll
     for (int e = 0; e < E; ++e) a[e] += f[e];
   }
@@ -240,7 +239,7 @@ template <typename T, int D>
 hipError_t route_impl(const Shape& s, const RouteArgs& a, hipStream_t st) {
   const unsigned bh = (unsigned)s.BH();
   hipLaunchKernelGGL((qbar_kernel<T, D>), dim3((s.n_b + 3) / 4, bh), dim3(256), 0, st,
-                     static_cast<const T*>(a.q), a.ws.qbar, s.n_b, (long long)s.N);
+                     static_cast<const T*>(a.q), a.ws.qbar, s.n_b, s.H, a.qs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned tiles = (unsigned)((s.n_b + 63) / 64);

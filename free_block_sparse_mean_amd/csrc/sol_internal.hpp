@@ -26,6 +26,23 @@ struct Shape {
   long long BH() const { return (long long)B * H; }
 };
 
+// Element strides of one [B][H][N][d] tensor whose rows of d values are
+// contiguous: element (ib, ih, t, c) sits at ib*b + ih*h + t*n + c. The default
+// (contiguous BHND) is {H*N*d, N*d, d}; BNHD is {N*H*d, d, H*d}.
+struct TStrides {
+  long long b, h, n;
+};
+inline TStrides contiguous_strides(const Shape& s) {
+  return TStrides{(long long)s.H * s.N * s.d, (long long)s.N * s.d, (long long)s.d};
+}
+struct IoStrides {
+  TStrides q, k, v, o;
+};
+inline IoStrides contiguous_io(const Shape& s) {
+  const TStrides c = contiguous_strides(s);
+  return IoStrides{c, c, c, c};
+}
+
 struct Workspace {
   float* kbar_t;    // [BH][d][n_b_pad]
   float* kbar;      // [BH][n_b][d]
@@ -73,12 +90,14 @@ struct FusedArgs {
   uint64_t* item_clock;
   const uint64_t* mask_in;   // non-null: caller-given selection, no routing and no correction
   int text_blocks;           // joint attention: the last text_blocks blocks are text (always exact)
+  IoStrides io;              // element strides of q, k, v and out
 };
 
 // Routing baselines with a materialized proxy map (route.hip).
 enum RouteMode : int { kRouteThreshold = 0, kRouteTopK = 1, kRouteTopP = 2 };
 struct RouteArgs {
   const void* q;
+  TStrides qs;         // element strides of q
   Workspace ws;        // pre-pass summaries of K (kbar) and room for qbar
   int mode;
   float beta;
@@ -92,8 +111,8 @@ struct RouteArgs {
 };
 
 // Each returns the first HIP error of its launches (hipSuccess otherwise).
-hipError_t launch_prepass(const Shape& s, Dtype dt, const void* k, const void* v,
-                          const Workspace& ws, hipStream_t stream);
+hipError_t launch_prepass(const Shape& s, Dtype dt, const void* k, const void* v, const TStrides& ks,
+                          const TStrides& vs, const Workspace& ws, hipStream_t stream);
 hipError_t launch_fused(const Shape& s, Dtype dt, const FusedArgs& a, hipStream_t stream);
 hipError_t launch_route(const Shape& s, Dtype dt, const RouteArgs& a, hipStream_t stream);
 

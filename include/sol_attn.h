@@ -23,7 +23,8 @@
  * exact virtual-token form are this library's reading of those passages.
  *
  * Tensor layout: q, k, v, out are contiguous [B][H][N][d] arrays in device
- * memory, all of one dtype (bfloat16 by default, float32 with SOL_F32).
+ * memory, all of one dtype (bfloat16 by default, float32 with SOL_F32);
+ * sol_attn_fwd_strided also takes other strides (e.g. [B][N][H][d]).
  * N must be a multiple of 64 (no partial block), 64 <= N <= 262144, and
  * d must be 64 or 128. Softmax scale is 1/sqrt(d).
  *
@@ -48,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SOL_ATTN_ABI_VERSION 2
+#define SOL_ATTN_ABI_VERSION 3
 
 typedef enum sol_status {
   SOL_OK = 0,
@@ -228,6 +229,34 @@ sol_status sol_attn_fwd_ex(const void* q, const void* k, const void* v, void* ou
                            int B, int H, int N, int d, float beta, unsigned flags,
                            void* hip_stream, void* workspace, size_t ws_bytes,
                            const sol_debug* dbg);
+
+/* Element strides of one logical [B][H][N][d] tensor whose d values per row
+ * are contiguous: element (ib, ih, t, c) is at ib*b + ih*h + t*n + c.
+ * Contiguous [B][H][N][d] is {H*N*d, N*d, d}; [B][N][H][d] is {N*H*d, d, H*d};
+ * one slice of a packed [B][N][3][H][d] projection is {3*N*H*d, d, 3*H*d}. */
+typedef struct sol_strides {
+  int64_t b, h, n;
+} sol_strides;
+
+/* sol_attn_fwd_ex for tensors in other layouts, so that the kernel drops in
+ * where a pipeline keeps its projections (the agihunt.info page on the paper
+ * presents the method as a drop-in, training-free replacement of the
+ * attention kernel; closing paragraphs). The arithmetic and the result are
+ * those of sol_attn_fwd_ex on the same logical tensors, bit for bit.
+ *   q_strides, k_strides, v_strides, out_strides: strides of each tensor, or
+ *     NULL for contiguous [B][H][N][d]. Every stride of a dimension longer
+ *     than 1 must be positive; every stride must be a multiple of 8 elements
+ *     (bf16) or 4 (fp32), and n must be below 2^24, else SOL_ERR_INVALID_ARG.
+ *     The out rows must not overlap one another or the inputs (not checked
+ *     beyond n >= d).
+ *   q, k, v, out: 16-byte aligned device pointers (else SOL_ERR_INVALID_ARG).
+ * Other arguments, workspace size and errors as sol_attn_fwd_ex. */
+sol_status sol_attn_fwd_strided(const void* q, const void* k, const void* v, void* out,
+                                int B, int H, int N, int d, const sol_strides* q_strides,
+                                const sol_strides* k_strides, const sol_strides* v_strides,
+                                const sol_strides* out_strides, float beta, unsigned flags,
+                                void* hip_stream, void* workspace, size_t ws_bytes,
+                                const sol_debug* dbg);
 
 /* Whole forward on the null stream of the current device with a library-owned
  * workspace (allocated on first use, grown when needed, held until the

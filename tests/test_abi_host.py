@@ -126,3 +126,27 @@ def test_joint_validation(lib):
     assert lib.sol_attn_fused_joint(p, p, p, p, 1, 1, 4096, 64, 1.0, 0, 65, p, big, None, None) == 1
     assert "text_blocks" in lib.sol_last_error().decode()
     assert lib.sol_attn_fused_joint(p, p, p, p, 1, 1, 4096, 64, 1.0, 0, 3, p, 10, None, None) == 5
+
+
+def test_strided_validation(lib):
+    from free_block_sparse_mean_amd.binding import sol_strides
+    p = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    big = 1 << 30
+    B, H, N, d = 1, 2, 4096, 64
+    bnhd = sol_strides(N * H * d, d, H * d)
+    call = lambda q=p, sq=None, sk=None, sv=None, so=None, flags=0, ws=big: lib.sol_attn_fwd_strided(
+        q, p, p, p, B, H, N, d, sq, sk, sv, so, 1.0, flags, None, p, ws, None)
+    ref = lambda s: ctypes.byref(s)
+    # valid strides reach the workspace check (error 5), invalid ones stop before it (error 1)
+    assert call(sq=ref(bnhd), sk=ref(bnhd), sv=ref(bnhd), so=ref(bnhd), ws=10) == 5
+    assert call(sq=ref(sol_strides(0, d, H * d)), ws=10) == 5          # b stride unused when B = 1
+    assert call(q=ctypes.c_void_p(24)) == 1
+    assert "aligned" in lib.sol_last_error().decode()
+    assert call(sq=ref(sol_strides(N * H * d, d, H * d + 4))) == 1     # not 16-byte rows (bf16)
+    assert "multiple of 8" in lib.sol_last_error().decode()
+    assert call(sq=ref(sol_strides(N * H * d, d, H * d + 4)), flags=1, ws=10) == 5   # fp32: 4 suffice
+    assert call(sk=ref(sol_strides(N * H * d, 0, H * d))) == 1        # h stride 0 with H = 2
+    assert call(sv=ref(sol_strides(N * H * d, d, -H * d))) == 1
+    assert call(sq=ref(sol_strides(N * H * d, d, 1 << 24))) == 1
+    assert call(so=ref(sol_strides(N * H * d, d, 8))) == 1              # out rows would overlap
+    assert "at least d" in lib.sol_last_error().decode()

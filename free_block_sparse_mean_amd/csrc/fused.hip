@@ -814,6 +814,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       unsigned keep = 0;                                                          \
       _Pragma("unroll") for (int g = 0; g < kGMax; ++g)                           \
         if (g < nG) keep |= (unsigned)((masks[g * n_words + (j >> 6)] >> (j & 63)) & 1ull) << g; \
+      keep = __builtin_amdgcn_readfirstlane(keep);   /* uniform: scalar tests */  \
       const int nj = union_next(j);                                               \
       /* this lane's loads of tile j have landed; the tile loop writes LDS  */    \
       /* only through those loads and every read of the other buffer was    */    \

@@ -857,7 +857,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (c + 1 < n_words)                                                      \
           issue_tile<D>(NEXTB, Kbs + (size_t)(c + 1) * 64 * D, dl.kc_off, 4096, Vbs + (size_t)(c + 1) * D * 64, dl); \
         _Pragma("unroll") for (int g = 0; g < kGMax; ++g) {                       \
-          const uint64_t ex = g < nG ? (masks[g * n_words + c] | pad) : ~0ull;    \
+          uint64_t ex = g < nG ? (masks[g * n_words + c] | pad) : ~0ull;          \
+          ex = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ex >> 32)) << 32) | \
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ex);   /* uniform */ \
           if (ex != ~0ull) tile_bf16<D, true>(sts[g], CURB, lofs, ex);            \
         }                                                                         \
         ++c;                                                                      \

@@ -282,7 +282,11 @@ def test_row_correction_exact_for_constant_key_blocks(dtype, gpu_lib):
         r = pu.run_gpu(qt.cuda(), kt.cuda(), vt.cuda(), beta, gpu_lib.SOL_CORRECTION_ROW, gpu_lib)
         got = r["out"][0, 0].numpy()
         rel, mab = (pu.BF16_REL_L2, pu.BF16_MAX_ABS) if dtype == BF else (pu.F32_REL_L2, pu.F32_MAX_ABS)
-        assert 0 < r["mask"].sum() < nb * nb
+        m = r["mask"][0, 0].numpy()
+        assert 0 < m.sum() < nb * nb
+        # rows that keep key block 31 and leave some of blocks 32..63 to the
+        # correction: the two 32-bit halves of a 64-bit exclusion word both matter
+        assert (m[:, 31] & ~m[:, 32:64].all(1)).any()
         assert pu.rel_l2(got, dense) <= rel and float(np.abs(got - dense).max()) <= mab
 
 

@@ -87,7 +87,7 @@ template <typename T, int D> struct Geom;
 // bf16: K tile [64][D] and V^T tile [D][64], unpadded; 16-byte chunks are
 // placed with an XOR swizzle so the MFMA operand reads hit distinct LDS banks.
 // Two buffers: the next kept tile is loaded straight into LDS
-// (global_load_lds_dwordx4) while the current one is computed.
+// (buffer_load_dwordx4 ... lds) while the current one is computed.
 template <int D> struct Geom<__bf16, D> {
   static constexpr int kKBytes = 64 * D * 2;
   static constexpr int kVBytes = D * 64 * 2;
@@ -262,17 +262,23 @@ template <int D>
 __device__ __forceinline__ void issue_tile(unsigned char* buf, const __bf16* Ksrc, int k_off, long long k_slab,
                                            const __bf16* Vsrc, const DmaLane& dl) {
   constexpr int NI = D / 32;   // slabs per region
-  const unsigned char* Kj = reinterpret_cast<const unsigned char*>(Ksrc);   // 64 rows of D
-  const unsigned char* Vj = reinterpret_cast<const unsigned char*>(Vsrc);   // [D][64]
+  // Buffer-form loads: a scalar descriptor per region (base = the tile, size =
+  // the tile's extent), this lane's fixed 32-bit offset and a scalar slab
+  // offset, so the addresses need no per-lane arithmetic. The 4th descriptor
+  // word selects 32-bit untyped data; accesses past the size read zeros.
+  constexpr int kRsrcWord3 = 0x00020000;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Ksrc), (short)0, (int)(NI * k_slab), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Vsrc), (short)0, NI * 4096, kRsrcWord3);
 #pragma unroll
   for (int i = 0; i < NI; ++i)
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(Kj + k_off + i * k_slab),
-                                     (lds_ptr_t*)(buf + i * 4096 + dl.wave_lds), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t*)(buf + i * 4096 + dl.wave_lds), 16, (unsigned)k_off,
+                                             (unsigned)(i * k_slab), 0, 0);
 #pragma unroll
   for (int i = 0; i < NI; ++i)
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(Vj + dl.v_off + i * 4096),
-                                     (lds_ptr_t*)(buf + Geom<__bf16, D>::kKBytes + i * 4096 + dl.wave_lds),
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t*)(buf + Geom<__bf16, D>::kKBytes + i * 4096 + dl.wave_lds),
+                                             16, (unsigned)dl.v_off, (unsigned)(i * 4096), 0, 0);
 }
 
 // fp32: stage the K and V tiles of key block j in LDS (synchronously)
@@ -793,16 +799,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       zero_state<T, D>(sts[g]);
       if (g < nG) load_q<T, D>(sts[g], Qh + ((long long)(qi0 + g) * kBlock + row) * p.qs.n, lane);
     }
-    auto union_next = [&](int j) -> int {   // next key block after j kept by any block
-      for (int wi = (j + 1) >> 6; wi < n_words; ++wi) {
-        uint64_t word = 0;
+    // The walk keeps the G blocks' mask words of one 64-block word index (cw)
+    // and their union in scalar registers; LDS is read again only when the
+    // walk moves on to the next word.
+    uint64_t wm[kGMax];
+    uint64_t uw = 0;
+    int cw = -1;
+    auto load_word = [&](int wi) {
+      uw = 0;
 #pragma unroll
-        for (int g = 0; g < kGMax; ++g)
-          if (g < nG) word |= masks[g * n_words + wi];
-        if (wi == ((j + 1) >> 6)) word &= ~0ull << ((j + 1) & 63);
-        if (word) return wi * 64 + (int)__builtin_ctzll(word);
+      for (int g = 0; g < kGMax; ++g) {
+        const uint64_t x = g < nG ? masks[g * n_words + wi] : 0ull;
+        wm[g] = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32) |
+                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
+        uw |= wm[g];
       }
-      return -1;
+      cw = wi;
+    };
+    auto union_next = [&](int j) -> int {   // next key block after j kept by any block
+      int wi = (j + 1) >> 6;
+      if (wi >= n_words) return -1;
+      if (wi != cw) load_word(wi);
+      uint64_t word = uw & (~0ull << ((j + 1) & 63));
+      while (!word) {
+        if (++wi >= n_words) return -1;
+        load_word(wi);
+        word = uw;
+      }
+      return wi * 64 + (int)__builtin_ctzll(word);
     };
     const __bf16* Vt = p.vt + (size_t)bh * n_b * D * 64;
 // s_waitcnt vmcnt(0) through the builtin, so the compiler's own wait tracking
@@ -811,10 +835,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #define SOL_WAIT_VM() __builtin_amdgcn_s_waitcnt(0xF70)
 #define SOL_STEP(CURB, NEXTB)                                                     \
     {                                                                             \
+      /* j lies in word cw (union_next found it there) */                       \
       unsigned keep = 0;                                                          \
       _Pragma("unroll") for (int g = 0; g < kGMax; ++g)                           \
-        if (g < nG) keep |= (unsigned)((masks[g * n_words + (j >> 6)] >> (j & 63)) & 1ull) << g; \
-      keep = __builtin_amdgcn_readfirstlane(keep);   /* uniform: scalar tests */  \
+        keep |= (unsigned)((wm[g] >> (j & 63)) & 1ull) << g;                      \
       const int nj = union_next(j);                                               \
       /* this lane's loads of tile j have landed; the tile loop writes LDS  */    \
       /* only through those loads and every read of the other buffer was    */    \

@@ -361,7 +361,7 @@ def main() -> int:
         return 2
 
     if args.sweep:
-        return sweep([x for x in args.sweep.split(",") if x], max(3, args.steps // 2))
+        return sweep([x for x in args.sweep.split(",") if x], max(3, args.steps))
 
     if args.copy_calibration:
         n = 512 * 2 ** 20

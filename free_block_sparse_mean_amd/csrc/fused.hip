@@ -719,7 +719,91 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // ---- 4. correction: unselected blocks as 64 virtual tokens ----------------
-  if constexpr (CORR) {
+  if constexpr (CORR && kBF) {
+    // bf16 inputs: the weights w_gj = 2^(s_hat_gj log2e - c_g) of the
+    // unselected blocks are rounded to bf16 (the row sum L adds the same
+    // rounded weights), and A_g = 64 sum_j w_gj v_bar_j runs on MFMA against
+    // the bf16 tiles of v_bar^T that the pre-pass writes for the per-row
+    // correction (columns of key blocks in the P-operand order of the walk).
+    float c2[kGMax];
+#pragma unroll
+    for (int g = 0; g < kGMax; ++g) c2[g] = misc[kC2 + g];
+    const int nw64 = n_words * 64;
+    float wr[kGMax][kMaxBlocks / 256];
+    float lp[kGMax] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kMaxBlocks / 256; ++i) {
+      const int j = t + 256 * i;
+#pragma unroll
+      for (int g = 0; g < kGMax; ++g) {
+        float wj = 0.f;
+        if (j < n_b && g < nG) {
+          const bool keep = (masks[g * n_words + (j >> 6)] >> (j & 63)) & 1ull;
+          if (!keep && c2[g] != -INFINITY)
+            wj = (float)to_bf16(fast_exp2(shr[g][j] * kLog2e - c2[g]));
+        }
+        wr[g][i] = wj;
+        lp[g] += wj;
+      }
+    }
+    block_sum_n<kGMax>(lp, misc);   // barriers: every proxy row has been read
+    if (t < kGMax) misc[kL + t] = misc[kTot + t] * (float)kBlock;
+    // bf16 weights in the tile column order: key block 64c + r sits at column
+    // 64c + q(r), q the inverse of the column -> key map of v_bar^T tiles;
+    // rows 0, 1 in the first tile buffer, rows 2, 3 in the second (zero past n_b)
+    auto wrow = [&](int g) -> __bf16* {
+      return reinterpret_cast<__bf16*>(g < 2 ? sbufA : sbufB) + (g & 1) * nw64;
+    };
+#pragma unroll
+    for (int i = 0; i < kMaxBlocks / 256; ++i) {
+      const int j = t + 256 * i;
+      if (j < nw64) {
+        const int r = j & 63, h = r >> 5, r32 = r & 31;
+        const int q = r32 < 16 ? 32 * h + 8 * (r32 >> 2) + (r32 & 3)
+                               : 32 * h + 8 * ((r32 - 16) >> 2) + 4 + (r32 & 3);
+#pragma unroll
+        for (int g = 0; g < kGMax; ++g) wrow(g)[(j & ~63) + q] = to_bf16(wr[g][i]);
+      }
+    }
+    __syncthreads();
+    // A^T (d x 16 columns, column g < nG) += v_bar^T (d x 32 key blocks) W^T,
+    // k-steps of 32 key blocks dealt round-robin to the 4 waves
+    {
+      const int l16 = lane & 15, grp = lane >> 4;
+      const __bf16* vbt = p.vbar_t + (size_t)bh * n_words * D * 64;
+      f32x4 o[D / 16];
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const bf16x8 zero8 = {};
+      for (int ks = w; ks < 2 * n_words; ks += 4) {
+        const bf16x8 bw = l16 < nG ? *reinterpret_cast<const bf16x8*>(wrow(l16 < 4 ? l16 : 0) + 32 * ks + 8 * grp)
+                                   : zero8;
+        const __bf16* vrow = vbt + ((size_t)(ks >> 1) * D + l16) * 64 + 32 * (ks & 1) + 8 * grp;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(vrow + (size_t)dt * 16 * 64);
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw, o[dt], 0, 0, 0);
+        }
+      }
+      // lane holds A^T[16dt + 4 grp + i][g = l16]
+      if (l16 < nG) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[(w * kGMax + l16) * D + 16 * dt + 4 * grp + i] = o[dt][i] * (float)kBlock;
+      }
+    }
+    __syncthreads();
+    if (t < D) {
+#pragma unroll
+      for (int g = 0; g < kGMax; ++g) {
+        const float s = (acc[(0 * kGMax + g) * D + t] + acc[(1 * kGMax + g) * D + t]) +
+                        (acc[(2 * kGMax + g) * D + t] + acc[(3 * kGMax + g) * D + t]);
+        qa[t * kGMax + g] = s;   // q_bar is no longer needed: qa now holds A
+      }
+    }
+  } else if constexpr (CORR) {
     float c2[kGMax];
 #pragma unroll
     for (int g = 0; g < kGMax; ++g) c2[g] = misc[kC2 + g];

@@ -29,6 +29,15 @@
 namespace sol {
 namespace {
 
+// Chunk swizzle of row r of a staged V block (CH 16-byte chunks per row): the
+// transposing reads below gather keys k0 + c for the eight k0 of one output
+// chunk row (4 apart within each half of 32 keys); this maps them to eight
+// distinct chunk slots.
+template <int CH>
+__device__ __forceinline__ int vt_swz(int r) {
+  return ((r >> 2) ^ ((r >> 5) << 2)) & (CH - 1);
+}
+
 // One wave per key block: lane (rg, cc) sums rows rg, rg+RG, ... of 16-byte
 // column chunk cc for K and V, then the row groups are folded by xor-shuffles.
 // With WRITE_VT the wave also stages its V block in LDS and writes it back
@@ -58,17 +67,26 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const T* __restrict__ k
   float ak[E], av[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) { ak[e] = 0.f; av[e] = 0.f; }
-#pragma unroll 8
+  // every load of the block first (all 2 * RPL of them in flight: the LDS
+  // stage caps a CU at eight waves, so each wave keeps its whole block moving)
+  typename V::raw rkr[RPL], rvr[RPL];
+#pragma unroll
   for (int i = 0; i < RPL; ++i) {
     const int r = rg + RG * i;
-    const typename V::raw rv = reinterpret_cast<const typename V::raw*>(vb0 + (long long)r * vs.n)[cc];
+    rkr[i] = reinterpret_cast<const typename V::raw*>(kb0 + (long long)r * ks.n)[cc];
+    rvr[i] = reinterpret_cast<const typename V::raw*>(vb0 + (long long)r * vs.n)[cc];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) {
+    const int r = rg + RG * i;
     float fk[E], fv[E];
-    V::to_float(reinterpret_cast<const typename V::raw*>(kb0 + (long long)r * ks.n)[cc], fk);
-    V::to_float(rv, fv);
+    V::to_float(rkr[i], fk);
+    V::to_float(rvr[i], fv);
 #pragma unroll
     for (int e = 0; e < E; ++e) { ak[e] += fk[e]; av[e] += fv[e]; }
     if constexpr (WRITE_VT)
-      *reinterpret_cast<typename V::raw*>(&stage[wv][r * kPitch + cc * E]) = rv;
+      *reinterpret_cast<typename V::raw*>(&stage[wv][r * kPitch + (cc ^ vt_swz<CH>(r)) * E]) = rvr[i];
   }
 #pragma unroll
   for (int o = CH; o < 64; o <<= 1) {
@@ -95,18 +113,23 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const T* __restrict__ k
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // Output chunk (d, kc) is 8 bf16 of head dim d: keys k0..k0+3 then
     // k0+16..k0+19 with k0 = 32*(kc/4) + 4*(kc%4), the order in which a lane
-    // of the fused kernel holds P for one 16x16x32 MFMA k-step. Consecutive
-    // lanes take consecutive d, so the LDS column reads do not share banks.
+    // of the fused kernel holds P for one 16x16x32 MFMA k-step. Eight
+    // consecutive lanes write the eight chunks of one d (128 contiguous
+    // bytes), so each store covers 1 KB; the row swizzle of the staged block
+    // puts the eight keys a read instruction gathers for one d in distinct
+    // 16-byte slots (distinct LDS banks).
     __bf16* dst = vt + ((size_t)bh * n_b + j) * D * 64;
     for (int c = lane; c < D * 8; c += 64) {
-      const int d = c % D, kc = c / D;
+      const int d = c >> 3, kc = c & 7;
       const int k0 = 32 * (kc >> 2) + 4 * (kc & 3);
       uint32_t w[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const int ka = k0 + (h >> 1) * 16 + 2 * (h & 1);
-        const uint32_t lo = __builtin_bit_cast(unsigned short, stage[wv][ka * kPitch + d]);
-        const uint32_t hi = __builtin_bit_cast(unsigned short, stage[wv][(ka + 1) * kPitch + d]);
+        const uint32_t lo = __builtin_bit_cast(
+            unsigned short, stage[wv][ka * kPitch + ((d / E) ^ vt_swz<CH>(ka)) * E + (d % E)]);
+        const uint32_t hi = __builtin_bit_cast(
+            unsigned short, stage[wv][(ka + 1) * kPitch + ((d / E) ^ vt_swz<CH>(ka + 1)) * E + (d % E)]);
         w[h] = lo | (hi << 16);
       }
       *reinterpret_cast<uint4*>(dst + (size_t)d * 64 + kc * 8) = make_uint4(w[0], w[1], w[2], w[3]);

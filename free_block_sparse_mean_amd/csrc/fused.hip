@@ -320,10 +320,32 @@ template <int D> struct LaneOfs {
 // block means k_bar_j of 64 key blocks, each standing for 64 equal tokens
 // (base-2 logit + log2(64) = 6), values v_bar_j; key blocks whose bit is set
 // in `excl` (kept exactly, or past n_b) get weight zero.
-template <int D, bool VIRT = false>
+// XO: operand offsets of k-steps ks > 0 formed in the tile from those of
+// k-step 0 (4 fewer registers held across the walk, 4 more VALU per tile):
+// used where the register budget is tightest (the per-row correction).
+template <int D, bool VIRT = false, bool XO = false>
 __device__ __forceinline__ void tile_bf16(ExactState<__bf16, D>& st, const unsigned char* buf, const LaneOfs<D>& lo,
                                           uint64_t excl = 0) {
   using S = ExactState<__bf16, D>;
+  // The XOR swizzles make the chunk index of k-step ks that of k-step 0 with
+  // bits 2-3 flipped by ks, i.e. byte offset bits 6-7 (K) or bit 6 (V^T); the
+  // empty asm keeps the compiler from hoisting the derived offsets out of the
+  // walk.
+  int ko[S::KS], vo[2];
+  if constexpr (XO) {
+    int k0 = lo.k[0], v0 = lo.v[0];
+    asm volatile("" : "+v"(k0), "+v"(v0));
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) ko[ks] = k0 ^ (64 * ks);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      vo[ks] = Geom<__bf16, D>::kKBytes + ((v0 - Geom<__bf16, D>::kKBytes) ^ (64 * ks));
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) ko[ks] = lo.k[ks];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) vo[ks] = lo.v[ks];
+  }
   constexpr float kScale2 = inv_sqrt(D) * kLog2e;   // logit -> base-2 exponent
   constexpr float kOff = VIRT ? 6.0f : 0.0f;        // log2 of the multiplicity
   // S^T (64 keys x 16 queries): 4 key sub-tiles of 16 rows of D/8 chunks
@@ -335,14 +357,14 @@ __device__ __forceinline__ void tile_bf16(ExactState<__bf16, D>& st, const unsig
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    ka[0][kt] = *reinterpret_cast<const bf16x8*>(buf + lo.k[0] + kt * 16 * D * 2);
+    ka[0][kt] = *reinterpret_cast<const bf16x8*>(buf + ko[0] + kt * 16 * D * 2);
   }
 #pragma unroll
   for (int ks = 0; ks < S::KS; ++ks) {
     if (ks + 1 < S::KS) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        ka[(ks + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(buf + lo.k[ks + 1] + kt * 16 * D * 2);
+        ka[(ks + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(buf + ko[ks + 1] + kt * 16 * D * 2);
     }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -407,7 +429,7 @@ __device__ __forceinline__ void tile_bf16(ExactState<__bf16, D>& st, const unsig
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
     for (int dt = 0; dt < S::NACC; ++dt) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(buf + lo.v[ks] + dt * 2048);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(buf + vo[ks] + dt * 2048);
       st.oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[ks], st.oacc[dt], 0, 0, 0);
     }
   }
@@ -877,6 +899,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // it, compute tile j.
     const LaneOfs<D> lofs(lane);
     const DmaLane dl = dma_lane<D>(t, p.ks.n);
+    constexpr bool kXO = MODE == kModeCorrRow;   // register budget: see tile_bf16
     ExactState<T, D> sts[kGMax];
 #pragma unroll
     for (int g = 0; g < kGMax; ++g) {
@@ -934,7 +957,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (nj >= 0)                                                                \
         issue_tile<D>(NEXTB, Kh + (long long)nj * kBlock * p.ks.n, dl.k_off, dl.k_slab, Vt + (size_t)nj * D * 64, dl); \
       _Pragma("unroll") for (int g = 0; g < kGMax; ++g)                           \
-        if (keep & (1u << g)) tile_bf16<D>(sts[g], CURB, lofs);                   \
+        if (keep & (1u << g)) tile_bf16<D, false, kXO>(sts[g], CURB, lofs);      \
       j = nj;                                                                     \
     }
     int j = union_next(-1);
@@ -968,7 +991,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           uint64_t ex = g < nG ? (masks[g * n_words + c] | pad) : ~0ull;          \
           ex = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ex >> 32)) << 32) | \
                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ex);   /* uniform */ \
-          if (ex != ~0ull) tile_bf16<D, true>(sts[g], CURB, lofs, ex);            \
+          if (ex != ~0ull) tile_bf16<D, true, kXO>(sts[g], CURB, lofs, ex);       \
         }                                                                         \
         ++c;                                                                      \
       }

@@ -33,11 +33,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build libsolattn.so)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libsolattn.so next to this file; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+# The bf16 per-row-correction kernels: fused.hip once more, alone in a
+# translation unit built with the max-ILP scheduler (their register demand then
+# fits without spills; the other kernels are faster under the default one).
+ROW_TU_FLAGS = ["-DSOL_FUSED_ROW_TU", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+
+
+def _run(cmd, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,6 +49,21 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{out}")
     if out.strip() and verbose:
         print(out, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libsolattn.so next to this file; returns its path."""
+    tmp = LIB + ".tmp"
+    row_obj = os.path.join(PKG, "fused_row.tmp.o")
+    inc = ["-I", os.path.join(ROOT, "include")]
+    obj_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    try:
+        _run([hipcc(), *obj_flags, *ROW_TU_FLAGS, *inc, "-c", os.path.join(CSRC, "fused.hip"), "-o", row_obj],
+             verbose)
+        _run([hipcc(), *HIPCC_FLAGS, *inc, *[os.path.join(CSRC, s) for s in SOURCES], "-x", "none", row_obj, "-o", tmp], verbose)
+    finally:
+        if os.path.exists(row_obj):
+            os.remove(row_obj)
     os.replace(tmp, LIB)
     return LIB
 

@@ -1069,6 +1069,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+#ifdef SOL_FUSED_ROW_TU
+}  // namespace
+
+// This translation unit holds only the bf16 kernels of the per-row correction
+// (built with the max-ILP scheduler, under which their register demand fits
+// without spills; the other kernels run faster under the default one).
+const void* fused_row_kernel_bf16(int d) {
+  return d == 64 ? (const void*)fused_kernel<__bf16, 64, kModeCorrRow>
+                 : (const void*)fused_kernel<__bf16, 128, kModeCorrRow>;
+}
+
+}  // namespace sol
+#else
+
+template <typename T, int D>
+const void* kernel_for(const FusedArgs& a) {
+  if (a.mask_in) return (const void*)fused_kernel<T, D, kModeGiven>;
+  if (a.correction_row) {
+    if constexpr (std::is_same<T, __bf16>::value) return fused_row_kernel_bf16(D);   // own translation unit
+    else return (const void*)fused_kernel<T, D, kModeCorrRow>;
+  }
+  return a.correction ? (const void*)fused_kernel<T, D, kModeCorr> : (const void*)fused_kernel<T, D, kModeRoute>;
+}
+
 template <typename T, int D>
 hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
   const FusedGeom g = fused_geom(s, std::is_same<T, __bf16>::value ? Dtype::BF16 : Dtype::F32);
@@ -1091,10 +1115,7 @@ hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
   p.mask_in = a.mask_in;
   p.text_blocks = a.text_blocks;
   const dim3 grid((unsigned)(8 * g.per_xcd * s.BH()));
-  const void* fn = a.mask_in          ? (const void*)fused_kernel<T, D, kModeGiven>
-                   : a.correction_row ? (const void*)fused_kernel<T, D, kModeCorrRow>
-                   : a.correction     ? (const void*)fused_kernel<T, D, kModeCorr>
-                                      : (const void*)fused_kernel<T, D, kModeRoute>;
+  const void* fn = kernel_for<T, D>(a);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
   if (e != hipSuccess) return e;
   void* args[] = {&p};
@@ -1130,3 +1151,4 @@ hipError_t launch_fused(const Shape& s, Dtype dt, const FusedArgs& a, hipStream_
 }
 
 }  // namespace sol
+#endif

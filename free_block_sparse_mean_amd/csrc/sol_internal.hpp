@@ -114,6 +114,9 @@ struct RouteArgs {
 hipError_t launch_prepass(const Shape& s, Dtype dt, const void* k, const void* v, const TStrides& ks,
                           const TStrides& vs, const Workspace& ws, hipStream_t stream);
 hipError_t launch_fused(const Shape& s, Dtype dt, const FusedArgs& a, hipStream_t stream);
+// The bf16 per-row-correction fused kernel for head dim d (64 or 128), compiled
+// in a translation unit of its own (fused.hip with SOL_FUSED_ROW_TU).
+const void* fused_row_kernel_bf16(int d);
 hipError_t launch_route(const Shape& s, Dtype dt, const RouteArgs& a, hipStream_t stream);
 
 

@@ -46,7 +46,14 @@ def kept_flop(w, kept_blocks: int) -> float:
 
 
 def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of a source file's code: comments and whitespace do not count, so a
+    counter summary stays valid across edits that leave the compiled kernel as it was."""
+    import re
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+    text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+    code = " ".join(text.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_from_profile():

@@ -22,25 +22,33 @@
 //      query blocks; the strict test against tau folded into 64-bit wave
 //      ballots, one word per 64 key blocks, kept in LDS (never in HBM);
 //   4. correction for the unselected blocks of each query block: own running
-//      max c, weights w_j = exp(s_hat_j - c), L = 64 sum w_j, A = sum w_j vsum_j,
-//      each vsum row loaded once for all G blocks;
-//   5. inner loop over the set bits of the G blocks, one flat sequence of
-//      (block, key block) tiles: the K tile and the transposed V tile of the
-//      next tile are loaded into registers while the current one is computed
-//      from LDS; per wave 16 query rows x 64 keys, S^T = K Q^T and
-//      O^T += V^T P^T on v_mfma_f32_16x16x32_bf16, online softmax in base 2
-//      in fp32, P rounded to bf16;
+//      max c, weights w_j = exp(s_hat_j - c), L = 64 sum w_j, A = sum w_j vsum_j;
+//      for bf16 inputs the weights are rounded to bf16 and A runs on MFMA
+//      against bf16 tiles of v_bar^T (fp32: each vsum row loaded once for all
+//      G blocks);
+//   5. inner loop over the union of the G blocks' kept sets, in ascending
+//      key-block order: each union tile's K and transposed V are loaded once,
+//      straight from global memory into LDS, and computed for every block
+//      that keeps it; two LDS buffers, so the next union tile loads while the
+//      current one is computed. Each wave holds 16 query rows of every block;
+//      S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16, online
+//      softmax in base 2 in fp32, P rounded to bf16;
 //   6. per query block: out = (O 2^(m-M) + A 2^(c-M)) / (l 2^(m-M) + L 2^(c-M)).
 // Each lane owns one query row (lane % 16) of its wave and a quarter of the
-// keys / head dims (lane / 16): row statistics need two xor-shuffles and the
-// rescale is lane-local.
+// keys / head dims (lane / 16): row statistics need two permlane swaps and
+// the rescale is lane-local.
 //
-// Workgroups are mapped so that consecutive work items (neighbouring query
-// blocks of one head, which keep largely the same key blocks) run on the
-// same XCD and share its L2.
+// Workgroups are mapped head-synchronously: all XCDs work on the same head at
+// a time (its K and V^T stay in the shared Infinity Cache), each XCD on a
+// contiguous run of its query groups (neighbouring query blocks, which keep
+// largely the same key blocks, share that XCD's L2).
 //
 // Bound: bf16 MFMA on the kept tiles (4*64*64*d flop per kept block); the
 // summary scan and the correction read n_b*d*4 bytes each per G query blocks.
+//
+// Compiled twice: the bf16 kernels of the per-row correction are built alone
+// in a translation unit of their own (SOL_FUSED_ROW_TU) with another
+// scheduler, every other kernel in the main one.
 //
 // The float32 instantiation (small problems, tighter tolerance) keeps the same
 // routing and correction and computes the kept tiles with fp32 VALU dot

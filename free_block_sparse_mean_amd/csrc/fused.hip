@@ -53,6 +53,7 @@
 // The float32 instantiation (small problems, tighter tolerance) keeps the same
 // routing and correction and computes the kept tiles with fp32 VALU dot
 // products from LDS-staged K and V, without prefetch.
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -78,6 +79,9 @@ struct FusedParams {
   const float* kcov;
   int n_b, n_b_pad, n_words, G, n_groups;
   long long BH, per_xcd;   // per_xcd: work items of one head given to each XCD
+  long long n_static_wg;   // workgroups of the statically mapped heads; the rest are queue workers
+  int dyn_heads;           // the last dyn_heads heads' work items form the queue
+  int qslot;               // this launch's queue counter in kQueue (zeroed before it)
   long long N;
   int H;
   TStrides qs, ks, vs, os;   // element strides of q, k, v and out (rows of d are contiguous)
@@ -90,6 +94,18 @@ struct FusedParams {
   const uint64_t* mask_in;   // caller-given selection (kModeGiven), [BH][n_b][n_words]
   int text_blocks;           // the last text_blocks blocks are text: always kept, dense rows
 };
+
+// Work-item queue counters, one per launch in flight (slots taken round-robin
+// by the host, each zeroed by queue_reset_kernel on the launch's stream just
+// before the launch): static device memory, nothing is allocated, and the
+// workspace stays read-only for the fused pass. Each translation unit that
+// holds fused kernels has its own pool.
+constexpr int kQueueSlots = 256;
+__device__ unsigned int kQueue[kQueueSlots];
+
+__global__ void queue_reset_kernel(int slot) {
+  if (threadIdx.x == 0) kQueue[slot] = 0u;
+}
 
 template <typename T, int D> struct Geom;
 // bf16: K tile [64][D] and V^T tile [D][64], unpadded; 16-byte chunks are
@@ -550,16 +566,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int n_b = p.n_b, nbp = p.n_b_pad, n_words = p.n_words;
 
-  // XCD-aware mapping: the hardware deals workgroups round-robin over the 8
-  // XCDs. Each head's n_groups work items are cut into 8 contiguous runs, run
-  // x going to XCD x, and heads are taken in order: all XCDs work on the same
-  // head at a time (its K and V^T stay in the shared Infinity Cache) and each
-  // XCD's L2 sees neighbouring query blocks, which keep similar key blocks.
+  // Work items (G consecutive query blocks of one head). The first
+  // BH - dyn_heads heads are mapped statically and XCD-aware: the hardware
+  // deals workgroups round-robin over the 8 XCDs; each head's n_groups items
+  // are cut into 8 contiguous runs, run x going to XCD x, and heads are taken
+  // in order, so all XCDs work on the same head at a time (its K and V^T stay
+  // in the shared Infinity Cache) and each XCD's L2 sees neighbouring query
+  // blocks, which keep similar key blocks. The items of the last dyn_heads
+  // heads form a queue served by the remaining workgroups (workers, twice as
+  // many as those items): each takes at most one item from a device counter,
+  // so an XCD that finishes its static share early starts its workers early
+  // and takes more of the end of the launch; workers that find the queue
+  // empty leave at once.
+  __shared__ int item_slot;
   const long long wgid = blockIdx.x;
-  const long long r = wgid >> 3;
-  const long long bh = r / p.per_xcd;
-  const int grp_id = (int)((wgid & 7) * p.per_xcd + (r - bh * p.per_xcd));
-  if (bh >= p.BH || grp_id >= p.n_groups) return;   // uniform over the workgroup
+  long long bh;
+  int grp_id;
+  if (wgid < p.n_static_wg) {
+    const long long r = wgid >> 3;
+    bh = r / p.per_xcd;
+    grp_id = (int)((wgid & 7) * p.per_xcd + (r - bh * p.per_xcd));
+    if (bh >= p.BH - p.dyn_heads || grp_id >= p.n_groups) return;   // uniform over the workgroup
+  } else {
+    if (t == 0) item_slot = (int)atomicAdd(&kQueue[p.qslot], 1u);
+    __syncthreads();
+    const int slot = __builtin_amdgcn_readfirstlane(item_slot);
+    if (slot >= p.dyn_heads * p.n_groups) return;   // queue empty: uniform over the workgroup
+    bh = p.BH - p.dyn_heads + slot / p.n_groups;
+    grp_id = slot % p.n_groups;
+  }
   const int qi0 = grp_id * p.G;
   const int nG = min(p.G, n_b - qi0);
   // optional work-item timing (debug): 100 MHz constant clock at start and end
@@ -1087,6 +1122,7 @@ const void* fused_row_kernel_bf16(int d) {
   return d == 64 ? (const void*)fused_kernel<__bf16, 64, kModeCorrRow>
                  : (const void*)fused_kernel<__bf16, 128, kModeCorrRow>;
 }
+const void* fused_row_reset_kernel() { return (const void*)queue_reset_kernel; }
 
 }  // namespace sol
 #else
@@ -1122,7 +1158,20 @@ hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
   p.item_clock = a.item_clock;
   p.mask_in = a.mask_in;
   p.text_blocks = a.text_blocks;
-  const dim3 grid((unsigned)(8 * g.per_xcd * s.BH()));
+  p.dyn_heads = g.dyn_heads;
+  p.n_static_wg = g.n_static_wg;
+  static std::atomic<unsigned> next_slot{0};
+  p.qslot = (int)(next_slot.fetch_add(1u, std::memory_order_relaxed) % kQueueSlots);
+  const dim3 grid((unsigned)(g.n_static_wg + g.workers));
+  // this launch's queue counter, zeroed by a kernel of the fused kernel's own
+  // translation unit (a kernel rather than a memset, so that the launch
+  // sequence can be captured in a graph)
+  const bool row_tu = std::is_same<T, __bf16>::value && a.correction_row && !a.mask_in;
+  const void* reset = row_tu ? fused_row_reset_kernel() : (const void*)queue_reset_kernel;
+  int slot_arg = p.qslot;
+  void* rargs[] = {&slot_arg};
+  hipError_t e0 = hipLaunchKernel(reset, dim3(1), dim3(64), rargs, 0, st);
+  if (e0 != hipSuccess) return e0;
   const void* fn = kernel_for<T, D>(a);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
   if (e != hipSuccess) return e;
@@ -1141,6 +1190,10 @@ FusedGeom geom_impl(const Shape& s) {
   g.n_groups = g.G ? (s.n_b + g.G - 1) / g.G : 0;
   g.items = s.BH() * g.n_groups;
   g.per_xcd = (g.n_groups + 7) / 8;
+  // the last head's items are dealt from a queue by twice as many workers
+  g.dyn_heads = s.BH() > 0 ? 1 : 0;
+  g.n_static_wg = 8 * g.per_xcd * (s.BH() - g.dyn_heads);
+  g.workers = 8 * ((2LL * g.dyn_heads * g.n_groups + 7) / 8);
   g.lds_bytes = L::bytes(g.G, s.n_words);
   return g;
 }

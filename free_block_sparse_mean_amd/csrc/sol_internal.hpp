@@ -70,6 +70,9 @@ struct FusedGeom {
   int n_groups;     // ceil(n_b / G) per head
   long long items;  // BH * n_groups
   long long per_xcd;  // ceil(n_groups / 8): work items of one head per XCD
+  int dyn_heads;      // trailing heads whose work items are dealt from a queue
+  long long n_static_wg;  // workgroups of the statically mapped heads
+  long long workers;      // queue workers (twice the queued items, at most one item each)
   int lds_bytes;
 };
 FusedGeom fused_geom(const Shape& s, Dtype dt);
@@ -117,6 +120,8 @@ hipError_t launch_fused(const Shape& s, Dtype dt, const FusedArgs& a, hipStream_
 // The bf16 per-row-correction fused kernel for head dim d (64 or 128), compiled
 // in a translation unit of its own (fused.hip with SOL_FUSED_ROW_TU).
 const void* fused_row_kernel_bf16(int d);
+// That translation unit's queue-slot reset kernel (its own slot pool).
+const void* fused_row_reset_kernel();
 hipError_t launch_route(const Shape& s, Dtype dt, const RouteArgs& a, hipStream_t stream);
 
 

@@ -132,6 +132,36 @@ def test_deterministic_and_stream(gpu_lib):
     assert torch.equal(out.float().cpu(), a["out"])
 
 
+def test_concurrent_fused_shared_workspace(gpu_lib):
+    """Fused calls on several streams at once, sharing one pre-pass workspace (which the
+    fused pass only reads), each give bit for bit the result of the same call alone: every
+    launch deals its queued work items from a counter of its own."""
+    w = wl.small("concurrent", 1, 8, 64 * 256, 128, grid=(4, 64, 64))
+    q, k, v = (t.cuda() for t in wl.make_qkv(w))
+    ws = gpu_lib.new_workspace(w.B, w.H, w.N, w.d)
+    gpu_lib.sol_block_summaries(k, v, ws)
+    qs = [q] + [torch.roll(q, shifts=64 * (i + 1), dims=2) for i in range(3)]   # other queries, same keys
+    flags = gpu_lib.SOL_CORRECTION
+    ref = []
+    for qi in qs:
+        o = torch.empty_like(qi)
+        gpu_lib.sol_attn_fused(qi, k, v, o, 1.0, flags, ws)
+        ref.append(o)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in qs]
+    outs = [[torch.empty_like(q) for _ in qs] for _ in range(3)]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, (qi, st) in enumerate(zip(qs, streams)):
+            with torch.cuda.stream(st):
+                gpu_lib.sol_attn_fused(qi, k, v, outs[rep][i], 1.0, flags, ws, stream=st)
+    torch.cuda.synchronize()
+    print("[concurrent] 4 streams x 3 launches", flush=True)
+    for rep in range(3):
+        for i in range(len(qs)):
+            assert torch.equal(outs[rep][i], ref[i]), f"stream {i}, launch {rep}"
+
+
 @pytest.mark.parametrize("w", [SMALL[0], SMALL[1], SMALL[2]], ids=lambda w: w.name)
 def test_prepass_summaries(w, gpu_lib):
     """k_bar, v sums, m and C of the pre-pass against the oracle's float64 block means."""

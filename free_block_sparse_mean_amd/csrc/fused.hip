@@ -1127,6 +1127,11 @@ const void* fused_row_reset_kernel() { return (const void*)queue_reset_kernel; }
 }  // namespace sol
 #else
 
+// Queue slot of the next launch: one counter for every fused launch of this
+// library (all instantiations, both translation units' pools), so that
+// launches in flight together never share a slot.
+std::atomic<unsigned> g_next_queue_slot{0};
+
 template <typename T, int D>
 const void* kernel_for(const FusedArgs& a) {
   if (a.mask_in) return (const void*)fused_kernel<T, D, kModeGiven>;
@@ -1160,8 +1165,7 @@ hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
   p.text_blocks = a.text_blocks;
   p.dyn_heads = g.dyn_heads;
   p.n_static_wg = g.n_static_wg;
-  static std::atomic<unsigned> next_slot{0};
-  p.qslot = (int)(next_slot.fetch_add(1u, std::memory_order_relaxed) % kQueueSlots);
+  p.qslot = (int)(g_next_queue_slot.fetch_add(1u, std::memory_order_relaxed) % kQueueSlots);
   const dim3 grid((unsigned)(g.n_static_wg + g.workers));
   // this launch's queue counter, zeroed by a kernel of the fused kernel's own
   // translation unit (a kernel rather than a memset, so that the launch

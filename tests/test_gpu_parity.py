@@ -133,32 +133,36 @@ def test_deterministic_and_stream(gpu_lib):
 
 
 def test_concurrent_fused_shared_workspace(gpu_lib):
-    """Fused calls on several streams at once, sharing one pre-pass workspace (which the
-    fused pass only reads), each give bit for bit the result of the same call alone: every
-    launch deals its queued work items from a counter of its own."""
-    w = wl.small("concurrent", 1, 8, 64 * 256, 128, grid=(4, 64, 64))
-    q, k, v = (t.cuda() for t in wl.make_qkv(w))
-    ws = gpu_lib.new_workspace(w.B, w.H, w.N, w.d)
-    gpu_lib.sol_block_summaries(k, v, ws)
-    qs = [q] + [torch.roll(q, shifts=64 * (i + 1), dims=2) for i in range(3)]   # other queries, same keys
+    """Fused calls on several streams at once, of two head dims (two kernel instantiations),
+    each group sharing one pre-pass workspace (which the fused pass only reads), give bit for
+    bit the result of the same call alone: every launch deals its queued work items from a
+    counter of its own."""
+    cases = []
+    for d in (128, 64):
+        w = wl.small(f"concurrent_d{d}", 1, 8, 64 * 256, d, grid=(4, 64, 64))
+        q, k, v = (t.cuda() for t in wl.make_qkv(w))
+        ws = gpu_lib.new_workspace(w.B, w.H, w.N, w.d)
+        gpu_lib.sol_block_summaries(k, v, ws)
+        for i in range(3):   # other queries, same keys and workspace
+            cases.append((torch.roll(q, shifts=64 * i, dims=2).contiguous(), k, v, ws))
     flags = gpu_lib.SOL_CORRECTION
     ref = []
-    for qi in qs:
+    for qi, k, v, ws in cases:
         o = torch.empty_like(qi)
         gpu_lib.sol_attn_fused(qi, k, v, o, 1.0, flags, ws)
         ref.append(o)
     torch.cuda.synchronize()
-    streams = [torch.cuda.Stream() for _ in qs]
-    outs = [[torch.empty_like(q) for _ in qs] for _ in range(3)]
+    streams = [torch.cuda.Stream() for _ in cases]
+    outs = [[torch.empty_like(c[0]) for c in cases] for _ in range(3)]
     torch.cuda.synchronize()
     for rep in range(3):
-        for i, (qi, st) in enumerate(zip(qs, streams)):
+        for i, ((qi, k, v, ws), st) in enumerate(zip(cases, streams)):
             with torch.cuda.stream(st):
                 gpu_lib.sol_attn_fused(qi, k, v, outs[rep][i], 1.0, flags, ws, stream=st)
     torch.cuda.synchronize()
-    print("[concurrent] 4 streams x 3 launches", flush=True)
+    print(f"[concurrent] {len(cases)} streams x 3 launches", flush=True)
     for rep in range(3):
-        for i in range(len(qs)):
+        for i in range(len(cases)):
             assert torch.equal(outs[rep][i], ref[i]), f"stream {i}, launch {rep}"
 
 

@@ -100,7 +100,7 @@ struct FusedParams {
 // before the launch): static device memory, nothing is allocated, and the
 // workspace stays read-only for the fused pass. Each translation unit that
 // holds fused kernels has its own pool.
-constexpr int kQueueSlots = 256;
+constexpr int kQueueSlots = 4096;
 __device__ unsigned int kQueue[kQueueSlots];
 
 __global__ void queue_reset_kernel(int slot) {

@@ -32,7 +32,11 @@
  * pointer after a call returns. Calls are asynchronous on the given HIP stream
  * (NULL = the null stream): buffers must stay alive until that stream has
  * finished the work. Nothing here allocates device memory except
- * sol_attn_fwd, which keeps one library-owned workspace per device.
+ * sol_attn_fwd, which keeps one library-owned workspace per device. The fused
+ * pass deals part of its work from a counter in the library's static device
+ * memory (16 KB per device), one of 4096 taken round-robin per launch: on
+ * one stream any number of launches may be queued; across streams, at most
+ * 4096 fused launches may be enqueued and not yet finished at a time.
  *
  * Errors: every entry point returns a sol_status and never aborts or throws.
  * Arguments are validated before any device call; on failure nothing has been

@@ -36,7 +36,10 @@
  * pass deals part of its work from a counter in the library's static device
  * memory (16 KB per device), one of 4096 taken round-robin per launch: on
  * one stream any number of launches may be queued; across streams, at most
- * 4096 fused launches may be enqueued and not yet finished at a time.
+ * 4096 fused launches may be enqueued and not yet finished at a time. A fused
+ * launch captured in a graph keeps its counter for every replay (the counter is
+ * cleared by a kernel of the graph), so such a graph must not be replayed
+ * concurrently with itself.
  *
  * Errors: every entry point returns a sol_status and never aborts or throws.
  * Arguments are validated before any device call; on failure nothing has been

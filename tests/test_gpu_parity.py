@@ -166,6 +166,38 @@ def test_concurrent_fused_shared_workspace(gpu_lib):
             assert torch.equal(outs[rep][i], ref[i]), f"stream {i}, launch {rep}"
 
 
+def test_graph_capture_replays(gpu_lib):
+    """The pre-pass and the fused pass captured in a HIP graph (its work-item queue counter
+    is cleared by a kernel, not a memset) replay bit for bit the eager result, several times,
+    with eager work and synchronisations between the replays."""
+    w = SMALL[1]
+    q, k, v = (t.cuda() for t in wl.make_qkv(w))
+    ws = gpu_lib.new_workspace(w.B, w.H, w.N, w.d)
+    flags = gpu_lib.SOL_CORRECTION
+    ref = torch.empty_like(q)
+    gpu_lib.sol_block_summaries(k, v, ws)
+    gpu_lib.sol_attn_fused(q, k, v, ref, 1.0, flags, ws)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            gpu_lib.sol_block_summaries(k, v, ws, stream=side)
+            gpu_lib.sol_attn_fused(q, k, v, out, 1.0, flags, ws, stream=side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.zero_()
+        scratch = torch.empty_like(q)
+        gpu_lib.sol_attn_fused(q, k, v, scratch, 0.5, flags, ws)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] replay {rep}", flush=True)
+        assert torch.equal(out, ref), f"replay {rep}"
+
+
 @pytest.mark.parametrize("w", [SMALL[0], SMALL[1], SMALL[2]], ids=lambda w: w.name)
 def test_prepass_summaries(w, gpu_lib):
     """k_bar, v sums, m and C of the pre-pass against the oracle's float64 block means."""

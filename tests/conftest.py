@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The HIP library binding; the test fails (not skips) if it cannot load on a GPU machine."""
+    """The HIP library binding; the test fails (not skips) if it cannot load on a machine with a GPU."""
     import torch
     if not torch.cuda.is_available():
         pytest.fail("GPU test collected on a host without a GPU")

@@ -126,3 +126,39 @@ def test_c5_error_against_dense(gpu_lib):
 
 def _dense_rows(qs, k, v):
     return orc.dense_attention(qs, k, v)
+
+
+MAX_N = 64 * 4096     # the library's largest sequence: 4096 blocks, 64 mask words per row
+MAX_CASES = [
+    (128, "bf16", "block"), (128, "bf16", "row"), (128, "bf16", "none"),
+    (64, "bf16", "block"), (64, "f32", "block"),
+]
+
+
+@pytest.mark.parametrize("d,dtype,corr", MAX_CASES, ids=[f"d{d}-{t}-{c}" for d, t, c in MAX_CASES])
+def test_max_sequence_length(d, dtype, corr, gpu_lib):
+    """N = 262144 (n_b = 4096), two heads: one taken by the statically mapped
+    workgroups, one dealt from the work-item queue. Every query block's selection
+    is checked against the oracle's routing; four query blocks per head (first,
+    last, densest, sparsest) against the oracle's outputs."""
+    print(f"case max N={MAX_N} d={d} {dtype} corr={corr}", flush=True)
+    _cache.clear()
+    torch.cuda.empty_cache()
+    w = wl.small(f"max_n_d{d}_{dtype}", 1, 2, MAX_N, d, dtype=dtype, grid=(64, 64, 64))
+    q, k, v = wl.make_qkv(w)
+    flags = {"block": gpu_lib.SOL_CORRECTION, "row": gpu_lib.SOL_CORRECTION_ROW, "none": 0}[corr]
+    beta = 1.5
+    out, kept, mask, tau = _run_like_bench(gpu_lib, q.cuda(), k.cuda(), v.cuda(), beta, flags)
+    assert torch.equal(kept, mask.sum(-1).to(torch.int32))
+    assert bool(torch.isfinite(out).all())
+    for h in range(w.H):
+        label = f"max N d={d} {dtype} {corr} h{h}"
+        r = pu.check_routing_head(q[0, h], k[0, h], mask[0, h].numpy(), tau[0, h].numpy(), beta, label)
+        kh = kept[0, h].numpy()
+        qb = sorted({0, w.n_blocks - 1, int(kh.argmax()), int(kh.argmin())})
+        res = pu.check_head(q[0, h], k[0, h], v[0, h], out[0, h].float().cpu().numpy(),
+                            mask[0, h].numpy(), tau[0, h].numpy(), beta, corr != "none", dtype,
+                            query_blocks=qb, label=label,
+                            correction_form="row" if corr == "row" else "block")
+        print(f"  {label}: density {r['density']:.4f} flips {r['flips']} "
+              f"rel-L2 {res['rel_l2_arith']:.2e} max-abs {res['max_abs_arith']:.2e}", flush=True)

@@ -139,66 +139,75 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const T* __restrict__ k
 
 // Partial first and second moments of the key summaries over one chunk of
 // kCovChunk blocks, in double; also writes the transposed summaries kbar_t.
+// blockIdx.z picks half of the D x D partial (rows z*D/2 ..); thread (ty, tx)
+// holds rows z*D/2 + ty + 16r and columns tx + 16s, so the 16 threads of a
+// row group read 16 consecutive doubles of a staged summary (no bank
+// conflicts). The staged tile is converted to double once.
 template <int D>
 __global__ __launch_bounds__(256) void moments_partial_kernel(const float* __restrict__ kbar,
                                                               float* __restrict__ kbar_t,
                                                               double* __restrict__ s1_part,
                                                               double* __restrict__ s2_part,
                                                               int n_b, int n_b_pad, int parts) {
-  constexpr int TJ = 32;       // key blocks staged per step
-  constexpr int R = D / 16;    // outputs per thread along each dimension
-  __shared__ float tile[TJ][D + 1];
+  constexpr int TJ = 32;            // key blocks staged per step
+  constexpr int RR = D / 32;        // rows per thread (half of the D rows over 16 row groups)
+  constexpr int RC = D / 16;        // columns per thread
+  constexpr int kPitch = D + 1;     // doubles per staged row: the transposing reads hit distinct banks
+  __shared__ double tile[TJ * kPitch];
   const int t = threadIdx.x, ty = t / 16, tx = t % 16;
   const long long bh = blockIdx.y;
-  const int part = blockIdx.x;
+  const int part = blockIdx.x, z = blockIdx.z;
   const int j0 = part * kCovChunk;
   const int j1 = min(n_b, j0 + kCovChunk);
-  double acc[R][R];
+  const int r0 = z * (D / 2);
+  double acc[RR][RC];
   double s1 = 0.0;
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < RR; ++r)
 #pragma unroll
-    for (int s = 0; s < R; ++s) acc[r][s] = 0.0;
+    for (int c = 0; c < RC; ++c) acc[r][c] = 0.0;
 
   for (int jb = j0; jb < j1; jb += TJ) {
     __syncthreads();
     for (int e = t; e < TJ * D; e += 256) {
       const int jj = e / D, c = e % D, j = jb + jj;
-      tile[jj][c] = j < j1 ? kbar[((size_t)bh * n_b + j) * D + c] : 0.f;
+      tile[jj * kPitch + c] = j < j1 ? (double)kbar[((size_t)bh * n_b + j) * D + c] : 0.0;
     }
     __syncthreads();
-    for (int e = t; e < TJ * D; e += 256) {
-      const int c = e / TJ, jj = e % TJ, j = jb + jj;
-      if (j < j1) kbar_t[((size_t)bh * D + c) * n_b_pad + j] = tile[jj][c];
+    // this half's columns of kbar_t (exact: the doubles came from floats)
+    for (int e = t; e < TJ * (D / 2); e += 256) {
+      const int c = r0 + e / TJ, jj = e % TJ, j = jb + jj;
+      if (j < j1) kbar_t[((size_t)bh * D + c) * n_b_pad + j] = (float)tile[jj * kPitch + c];
     }
     const int nj = min(TJ, j1 - jb);
     for (int jj = 0; jj < nj; ++jj) {
-      double a[R], b[R];
+      const double* row = tile + jj * kPitch;
+      double a[RR], b[RC];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        a[r] = (double)tile[jj][ty * R + r];
-        b[r] = (double)tile[jj][tx * R + r];
-      }
+      for (int r = 0; r < RR; ++r) a[r] = row[r0 + ty + 16 * r];
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int c = 0; c < RC; ++c) b[c] = row[tx + 16 * c];
 #pragma unroll
-        for (int s = 0; s < R; ++s) acc[r][s] += a[r] * b[s];
-      if (t < D) s1 += (double)tile[jj][t];
+      for (int r = 0; r < RR; ++r)
+#pragma unroll
+        for (int c = 0; c < RC; ++c) acc[r][c] += a[r] * b[c];
+      if (z == 0 && t < D) s1 += row[t];
     }
   }
-  // zero the row padding of kbar_t once per head
+  // zero this half's row padding of kbar_t once per head
   if (part == parts - 1) {
-    for (int e = t; e < D * (n_b_pad - n_b); e += 256) {
-      const int c = e / (n_b_pad - n_b), j = n_b + e % (n_b_pad - n_b);
+    const int pad = n_b_pad - n_b;
+    for (int e = t; e < (D / 2) * pad; e += 256) {
+      const int c = r0 + e / pad, j = n_b + e % pad;
       kbar_t[((size_t)bh * D + c) * n_b_pad + j] = 0.f;
     }
   }
   double* outp = s2_part + ((size_t)bh * parts + part) * D * D;
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < RR; ++r)
 #pragma unroll
-    for (int s = 0; s < R; ++s) outp[(size_t)(ty * R + r) * D + tx * R + s] = acc[r][s];
-  if (t < D) s1_part[((size_t)bh * parts + part) * D + t] = s1;
+    for (int c = 0; c < RC; ++c) outp[(size_t)(r0 + ty + 16 * r) * D + tx + 16 * c] = acc[r][c];
+  if (z == 0 && t < D) s1_part[((size_t)bh * parts + part) * D + t] = s1;
 }
 
 // m = (sum of the S1 partials) / n_b and C = (sum of the S2 partials) / n_b - m m^T,
@@ -261,7 +270,7 @@ hipError_t prepass_impl(const Shape& s, const void* k, const void* v, const TStr
                      s.n_b, s.H, ks, vs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((moments_partial_kernel<D>), dim3(s.cov_parts, bh), dim3(256), 0, st, ws.kbar,
+  hipLaunchKernelGGL((moments_partial_kernel<D>), dim3(s.cov_parts, bh, 2), dim3(256), 0, st, ws.kbar,
                      ws.kbar_t, ws.s1_part, ws.s2_part, s.n_b, s.n_b_pad, s.cov_parts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if constexpr (kVT) {

@@ -195,31 +195,35 @@ def prepass_report(w, pre_ms: float) -> dict:
 
 def cpu_baseline(w, q, k, v, beta: float, blocks_per_head: int, heads):
     """The oracle, untuned, on a bounded sample: `blocks_per_head` seeded query blocks of
-    each listed head. Returns the dense-equivalent TFLOP/s of the sampled rows."""
+    each listed head, on one host thread (numpy's BLAS limited to one thread, so `cores`
+    is exactly what it used; the oracle itself is a single Python loop over query
+    blocks). Returns the dense-equivalent TFLOP/s of the sampled rows."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
     from oracle import sol_oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
     rng = np.random.default_rng(1234)
     nb = w.N // 64
     per_block = 4.0 * 64 * w.N * w.d
     arrays = [(q[0, h].float().numpy(), k[0, h].float().numpy(), v[0, h].float().numpy()) for h in heads]
     picks = [np.sort(rng.choice(nb, size=blocks_per_head, replace=False)) for _ in heads]
-    t0 = time.perf_counter()
-    for (qh, kh, vh), qb in zip(arrays, picks):
-        orc.sol_attention_head(qh, kh, vh, beta, True, query_blocks=qb)
-    el = time.perf_counter() - t0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for (qh, kh, vh), qb in zip(arrays, picks):
+            orc.sol_attention_head(qh, kh, vh, beta, True, query_blocks=qb)
+        el = time.perf_counter() - t0
     n_blocks = blocks_per_head * len(heads)
     tflops = n_blocks * per_block / el / 1e12
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        nproc = os.cpu_count() or 1
     return {
-        "value": tflops, "unit": "TFLOP/s (dense-equivalent)", "cores": int(cores), "kind": "oracle",
+        "value": tflops, "unit": "TFLOP/s (dense-equivalent)", "cores": 1, "kind": "oracle",
+        "threads_used": 1, "host_cores_nproc": nproc, "host_cpu_count": os.cpu_count(),
         "cpu_model": cpu_model(),
         "sample": (f"{blocks_per_head} seeded query blocks x {len(heads)} heads of the "
                    f"{w.name} workload (B={w.B}, H={w.H}, N={w.N}, d={w.d}), beta={beta}, "
-                   f"correction on: {n_blocks} of {w.B * w.H * nb} query blocks"),
+                   f"correction on: {n_blocks} of {w.B * w.H * nb} query blocks, one host thread"),
         "seconds": el,
         "extrapolated_full_s": el * (w.B * w.H * nb) / n_blocks,
     }
@@ -363,7 +367,7 @@ def main() -> int:
     ap.add_argument("--no-correction", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-routing-study", action="store_true")
-    ap.add_argument("--cpu-blocks-per-head", type=int, default=128)
+    ap.add_argument("--cpu-blocks-per-head", type=int, default=24)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (for counter scaling)")
     ap.add_argument("--sweep", default="",

@@ -135,6 +135,42 @@ def _shape(q: torch.Tensor):
     return tuple(int(x) for x in q.shape)
 
 
+def _same_as(q: torch.Tensor, **others: torch.Tensor) -> None:
+    """Every named tensor has q's [B, H, N, d] shape, dtype and device."""
+    for name, t in others.items():
+        if tuple(t.shape) != tuple(q.shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, q has {tuple(q.shape)}")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} is {t.dtype}, q is {q.dtype}")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q is on {q.device}")
+
+
+def _check_out(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, numel: int,
+               device: torch.device) -> None:
+    """An optional per-call output: dtype, element count, device and contiguity."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements (got {t.numel()})")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_dbg(q: torch.Tensor, kept_per_row=None, mask_bits=None, tau=None, item_clock=None) -> None:
+    B, H, N, _ = _shape(q)
+    nb = N // BLOCK
+    rows = B * H * nb
+    _check_out(kept_per_row, "kept_per_row", torch.int32, rows, q.device)
+    _check_out(mask_bits, "mask_bits", torch.int64, rows * ((nb + 63) // 64), q.device)
+    _check_out(tau, "tau", torch.float32, rows, q.device)
+    _check_out(item_clock, "item_clock", torch.int64, rows * 2, q.device)
+
+
 def _dtype_flag(*ts: torch.Tensor) -> int:
     dts = {t.dtype for t in ts}
     if dts == {torch.bfloat16}:
@@ -148,6 +184,10 @@ def _dev(*ts: torch.Tensor) -> None:
     for t in ts:
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous device tensors")
+
+
+def _ws_bytes(workspace: torch.Tensor) -> int:
+    return workspace.numel() * workspace.element_size()
 
 
 def _stream(stream) -> int:
@@ -190,29 +230,32 @@ def workspace_views(ws: torch.Tensor, B: int, H: int, N: int, d: int) -> Dict[st
 
 def sol_block_summaries(k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor,
                         flags: int = 0, stream=None) -> None:
-    _dev(k, v, workspace)
     B, H, N, d = _shape(k)
+    _same_as(k, v=v)
+    _dev(k, v, workspace)
     flags |= _dtype_flag(k, v)
     _check(load_library().sol_block_summaries(k.data_ptr(), v.data_ptr(), B, H, N, d, flags,
-                                              workspace.data_ptr(), workspace.numel(),
+                                              workspace.data_ptr(), _ws_bytes(workspace),
                                               _stream(stream)))
 
 
 def sol_attn_fused(q, k, v, out, beta: float, flags: int, workspace: torch.Tensor, *,
                    kept_per_row=None, mask_bits=None, tau=None, item_clock=None, stream=None,
                    text_blocks: int = 0) -> None:
-    _dev(q, k, v, out, workspace)
     B, H, N, d = _shape(q)
+    _same_as(q, k=k, v=v, out=out)
+    _check_dbg(q, kept_per_row, mask_bits, tau, item_clock)
+    _dev(q, k, v, out, workspace)
     flags |= _dtype_flag(q, k, v, out)
     if text_blocks:
         _check(load_library().sol_attn_fused_joint(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d, float(beta), flags,
-            int(text_blocks), workspace.data_ptr(), workspace.numel(),
+            int(text_blocks), workspace.data_ptr(), _ws_bytes(workspace),
             _dbg(kept_per_row, mask_bits, tau, item_clock), _stream(stream)))
         return
     _check(load_library().sol_attn_fused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                          B, H, N, d, float(beta), flags, workspace.data_ptr(),
-                                         workspace.numel(), _dbg(kept_per_row, mask_bits, tau, item_clock),
+                                         _ws_bytes(workspace), _dbg(kept_per_row, mask_bits, tau, item_clock),
                                          _stream(stream)))
 
 
@@ -221,17 +264,25 @@ def sol_route(q, mode: int, workspace: torch.Tensor, proxy_map: torch.Tensor, ma
               flags: int = 0, stream=None) -> None:
     """Routing baseline with a materialized proxy map (float32 [B, H, n_b, n_b]); mask words
     int64 [B, H, n_b, W] written; the workspace must hold the pre-pass of the same K."""
-    _dev(q, workspace, proxy_map, mask_bits)
     B, H, N, d = _shape(q)
     nb = N // BLOCK
     if proxy_map.dtype != torch.float32 or proxy_map.numel() != B * H * nb * nb:
         raise ValueError("proxy_map must be float32 [B, H, n_b, n_b]")
     if mask_bits.dtype != torch.int64 or mask_bits.numel() != B * H * nb * ((nb + 63) // 64):
         raise ValueError("mask_bits must be int64 [B, H, n_b, ceil(n_b/64)]")
+    _check_out(proxy_map, "proxy_map", torch.float32, B * H * nb * nb, q.device)
+    _check_out(mask_bits, "mask_bits", torch.int64, B * H * nb * ((nb + 63) // 64), q.device)
+    _check_out(kept_per_row, "kept_per_row", torch.int32, B * H * nb, q.device)
+    if int(mode) == SOL_ROUTE_TOPK and topk_idx is not None:
+        # rows of top_k entries (only min(top_k, n_b) of each written)
+        if topk_idx.numel() < B * H * nb * max(int(top_k), 0):
+            raise ValueError(f"topk_idx must hold B*H*n_b*top_k = {B * H * nb * max(int(top_k), 0)} entries")
+        _check_out(topk_idx, "topk_idx", torch.int32, topk_idx.numel(), q.device)
+    _dev(q, workspace, proxy_map, mask_bits)
     flags |= _dtype_flag(q)
     ptr = lambda t: None if t is None else t.data_ptr()
     _check(load_library().sol_route(q.data_ptr(), B, H, N, d, flags, int(mode), float(beta), int(top_k),
-                                    float(top_p), workspace.data_ptr(), workspace.numel(),
+                                    float(top_p), workspace.data_ptr(), _ws_bytes(workspace),
                                     proxy_map.data_ptr(), mask_bits.data_ptr(), ptr(kept_per_row),
                                     ptr(topk_idx), _stream(stream)))
 
@@ -239,14 +290,16 @@ def sol_route(q, mode: int, workspace: torch.Tensor, proxy_map: torch.Tensor, ma
 def sol_attn_masked(q, k, v, out, mask_bits: torch.Tensor, flags: int, workspace: torch.Tensor, *,
                     kept_per_row=None, stream=None) -> None:
     """Block-sparse attention on a given selection (mask_bits: int64 [B, H, n_b, W] words)."""
-    _dev(q, k, v, out, mask_bits, workspace)
     B, H, N, d = _shape(q)
+    _same_as(q, k=k, v=v, out=out)
     if mask_bits.dtype != torch.int64 or mask_bits.numel() != B * H * (N // BLOCK) * ((N // BLOCK + 63) // 64):
         raise ValueError("mask_bits must be int64 [B, H, n_b, ceil(n_b/64)]")
+    _check_dbg(q, kept_per_row=kept_per_row, mask_bits=mask_bits)
+    _dev(q, k, v, out, mask_bits, workspace)
     flags |= _dtype_flag(q, k, v, out)
     _check(load_library().sol_attn_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                           B, H, N, d, mask_bits.data_ptr(), flags, workspace.data_ptr(),
-                                          workspace.numel(),
+                                          _ws_bytes(workspace),
                                           None if kept_per_row is None else kept_per_row.data_ptr(),
                                           _stream(stream)))
 
@@ -254,14 +307,17 @@ def sol_attn_masked(q, k, v, out, mask_bits: torch.Tensor, flags: int, workspace
 def sol_attn_fwd_ex(q, k, v, out, beta: float, flags: int, stream=None,
                     workspace: Optional[torch.Tensor] = None, *, kept_per_row=None,
                     mask_bits=None, tau=None, item_clock=None) -> None:
-    _dev(q, k, v, out)
     B, H, N, d = _shape(q)
+    _same_as(q, k=k, v=v, out=out)
+    _check_dbg(q, kept_per_row, mask_bits, tau, item_clock)
+    _dev(q, k, v, out)
     flags |= _dtype_flag(q, k, v, out)
     if workspace is None:
         workspace = new_workspace(B, H, N, d, q.device)
+    _dev(workspace)
     _check(load_library().sol_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                           B, H, N, d, float(beta), flags, _stream(stream),
-                                          workspace.data_ptr(), workspace.numel(),
+                                          workspace.data_ptr(), _ws_bytes(workspace),
                                           _dbg(kept_per_row, mask_bits, tau, item_clock)))
 
 
@@ -278,25 +334,37 @@ def sol_attn_fwd_strided(q, k, v, out, beta: float, flags: int, stream=None,
     """sol_attn_fwd_ex on [B, H, N, d] views of any strides (rows of d contiguous), e.g.
     x.transpose(1, 2) of a [B, N, H, d] tensor or slices of a packed QKV projection."""
     B, H, N, d = _shape(q)
-    for t in (k, v, out):
-        if tuple(t.shape) != (B, H, N, d):
-            raise ValueError("q, k, v and out must have the same [B, H, N, d] shape")
+    _same_as(q, k=k, v=v, out=out)
+    _check_dbg(q, kept_per_row, mask_bits, tau, item_clock)
     sq, sk, sv, so = _strides(q), _strides(k), _strides(v), _strides(out)
     flags |= _dtype_flag(q, k, v, out)
     if workspace is None:
         workspace = new_workspace(B, H, N, d, q.device)
     _check(load_library().sol_attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                                B, H, N, d, sq, sk, sv, so, float(beta), flags,
-                                               _stream(stream), workspace.data_ptr(), workspace.numel(),
+                                               _stream(stream), workspace.data_ptr(), _ws_bytes(workspace),
                                                _dbg(kept_per_row, mask_bits, tau, item_clock)))
 
 
 def sol_attn_fwd(q, k, v, out, beta: float, flags: int) -> None:
-    _dev(q, k, v, out)
+    """The whole forward on the null stream with the library's own workspace. The null
+    stream is made to wait for torch's current stream before the call, and the current
+    stream to wait for the null stream after it, so the call is ordered like any other
+    operation on the current stream (torch's side streams do not synchronise with the
+    null stream by themselves)."""
     B, H, N, d = _shape(q)
+    _same_as(q, k=k, v=v, out=out)
+    _dev(q, k, v, out)
     flags |= _dtype_flag(q, k, v, out)
+    cur = torch.cuda.current_stream(q.device)
+    null = torch.cuda.default_stream(q.device)
+    side = cur.cuda_stream != null.cuda_stream
+    if side:
+        null.wait_stream(cur)
     _check(load_library().sol_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                        B, H, N, d, float(beta), flags))
+    if side:
+        cur.wait_stream(null)
 
 
 def decode_mask(mask_bits: torch.Tensor, n_b: int) -> torch.Tensor:

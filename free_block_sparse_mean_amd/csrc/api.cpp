@@ -104,6 +104,41 @@ sol_status check_flags(unsigned flags) {
   return SOL_OK;
 }
 
+// Device pointers the kernels read or write with 16-byte vector accesses
+// (q, k, v, out), the workspace (arrays at 256-byte offsets, read as float4
+// and double) and the debug outputs (natural alignment of their elements).
+sol_status check_align(const void* p, size_t a, const char* name) {
+  if (p && reinterpret_cast<uintptr_t>(p) % a)
+    return fail(SOL_ERR_INVALID_ARG, "%s must be %zu-byte aligned", name, a);
+  return SOL_OK;
+}
+
+sol_status check_io_align(const void* q, const void* k, const void* v, const void* out) {
+  sol_status st;
+  if (q && (st = check_align(q, 16, "q")) != SOL_OK) return st;
+  if ((st = check_align(k, 16, "k")) != SOL_OK) return st;
+  if ((st = check_align(v, 16, "v")) != SOL_OK) return st;
+  if (out && (st = check_align(out, 16, "out")) != SOL_OK) return st;
+  return SOL_OK;
+}
+
+sol_status check_dbg_align(const sol_debug* dbg) {
+  if (!dbg) return SOL_OK;
+  sol_status st;
+  if ((st = check_align(dbg->kept_per_row, 4, "kept_per_row")) != SOL_OK) return st;
+  if ((st = check_align(dbg->mask_bits, 8, "mask_bits")) != SOL_OK) return st;
+  if ((st = check_align(dbg->tau, 4, "tau")) != SOL_OK) return st;
+  return check_align(dbg->item_clock, 8, "item_clock");
+}
+
+// A caller workspace: present, large enough for the shape, 256-byte aligned.
+sol_status check_workspace(const sol::Shape& s, const void* ws, size_t ws_bytes) {
+  const size_t need = sol::make_layout(s).total;
+  if (!ws || ws_bytes < need)
+    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, ws_bytes, ws ? "" : ", NULL");
+  return check_align(ws, 256, "workspace");
+}
+
 sol::Dtype dtype_of(unsigned flags) { return (flags & SOL_F32) ? sol::Dtype::F32 : sol::Dtype::BF16; }
 
 sol_status finish(unsigned flags, hipStream_t st) {
@@ -151,7 +186,9 @@ sol_status check_fused_args(const void* q, const void* k, const void* v, void* o
                             unsigned flags) {
   if (!q || !k || !v || !out) return fail(SOL_ERR_INVALID_ARG, "q, k, v and out must be non-null");
   if (isnan(beta)) return fail(SOL_ERR_INVALID_ARG, "beta is NaN");
-  return check_flags(flags);
+  sol_status st = check_flags(flags);
+  if (st != SOL_OK) return st;
+  return check_io_align(q, k, v, out);
 }
 
 // Strides of one tensor from the caller (NULL: contiguous), validated.
@@ -234,9 +271,8 @@ sol_status sol_block_summaries(const void* k, const void* v, int B, int H, int N
   if (st != SOL_OK) return st;
   if (!k || !v) return fail(SOL_ERR_INVALID_ARG, "k and v must be non-null");
   if ((st = check_flags(flags)) != SOL_OK) return st;
-  if (!workspace || ws_bytes < sol::make_layout(s).total)
-    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
-                ws_bytes, workspace ? "" : ", NULL");
+  if ((st = check_io_align(nullptr, k, v, nullptr)) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   if ((st = summaries_checked(s, k, v, flags, workspace, str)) != SOL_OK) return st;
   return finish(flags, str);
@@ -249,9 +285,8 @@ sol_status sol_attn_fused(const void* q, const void* k, const void* v, void* out
   sol_status st = check_shape(B, H, N, d, &s);
   if (st != SOL_OK) return st;
   if ((st = check_fused_args(q, k, v, out, beta, flags)) != SOL_OK) return st;
-  if (!workspace || ws_bytes < sol::make_layout(s).total)
-    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
-                ws_bytes, workspace ? "" : ", NULL");
+  if ((st = check_dbg_align(dbg)) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str)) != SOL_OK) return st;
   return finish(flags, str);
@@ -269,9 +304,10 @@ sol_status sol_attn_masked(const void* q, const void* k, const void* v, void* ou
   if ((st = check_flags(flags)) != SOL_OK) return st;
   if (flags & (SOL_CORRECTION | SOL_CORRECTION_ROW | SOL_DENSE))
     return fail(SOL_ERR_INVALID_ARG, "the given-mask mode takes neither SOL_CORRECTION(_ROW) nor SOL_DENSE");
-  if (!workspace || ws_bytes < sol::make_layout(s).total)
-    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
-                ws_bytes, workspace ? "" : ", NULL");
+  if ((st = check_io_align(q, k, v, out)) != SOL_OK) return st;
+  if ((st = check_align(mask_bits, 8, "mask_bits")) != SOL_OK) return st;
+  if ((st = check_align(kept_per_row, 4, "kept_per_row")) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   sol::FusedArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out;
@@ -309,9 +345,12 @@ sol_status sol_route(const void* q, int B, int H, int N, int d, unsigned flags, 
   if (mode == SOL_ROUTE_THRESHOLD && isnan(beta)) return fail(SOL_ERR_INVALID_ARG, "beta is NaN");
   if (mode == SOL_ROUTE_TOPP && !(topp == topp)) return fail(SOL_ERR_INVALID_ARG, "top_p is NaN");
   if (mode == SOL_ROUTE_TOPK && topk < 0) return fail(SOL_ERR_INVALID_ARG, "top_k is negative");
-  if (!workspace || ws_bytes < sol::make_layout(s).total)
-    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
-                ws_bytes, workspace ? "" : ", NULL");
+  if ((st = check_align(q, 16, "q")) != SOL_OK) return st;
+  if ((st = check_align(proxy_map, 4, "proxy_map")) != SOL_OK) return st;
+  if ((st = check_align(mask_bits, 8, "mask_bits")) != SOL_OK) return st;
+  if ((st = check_align(kept_per_row, 4, "kept_per_row")) != SOL_OK) return st;
+  if ((st = check_align(topk_idx, 4, "topk_idx")) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   sol::RouteArgs a;
   a.q = q;
@@ -341,9 +380,8 @@ sol_status sol_attn_fused_joint(const void* q, const void* k, const void* v, voi
   if ((st = check_fused_args(q, k, v, out, beta, flags)) != SOL_OK) return st;
   if (text_blocks < 0 || text_blocks > s.n_b)
     return fail(SOL_ERR_INVALID_ARG, "text_blocks must be in [0, n_b] (got %d, n_b %d)", text_blocks, s.n_b);
-  if (!workspace || ws_bytes < sol::make_layout(s).total)
-    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
-                ws_bytes, workspace ? "" : ", NULL");
+  if ((st = check_dbg_align(dbg)) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str, text_blocks)) != SOL_OK) return st;
   return finish(flags, str);
@@ -356,9 +394,8 @@ sol_status sol_attn_fwd_ex(const void* q, const void* k, const void* v, void* ou
   sol_status st = check_shape(B, H, N, d, &s);
   if (st != SOL_OK) return st;
   if ((st = check_fused_args(q, k, v, out, beta, flags)) != SOL_OK) return st;
-  if (!workspace || ws_bytes < sol::make_layout(s).total)
-    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
-                ws_bytes, workspace ? "" : ", NULL");
+  if ((st = check_dbg_align(dbg)) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   if ((st = summaries_checked(s, k, v, flags, workspace, str)) != SOL_OK) return st;
   if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str)) != SOL_OK) return st;
@@ -379,9 +416,8 @@ sol_status sol_attn_fwd_strided(const void* q, const void* k, const void* v, voi
   if ((st = take_strides(s, flags, k_strides, k, "k", false, &io.k)) != SOL_OK) return st;
   if ((st = take_strides(s, flags, v_strides, v, "v", false, &io.v)) != SOL_OK) return st;
   if ((st = take_strides(s, flags, out_strides, out, "out", true, &io.o)) != SOL_OK) return st;
-  if (!workspace || ws_bytes < sol::make_layout(s).total)
-    return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", sol::make_layout(s).total,
-                ws_bytes, workspace ? "" : ", NULL");
+  if ((st = check_dbg_align(dbg)) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   if ((st = summaries_checked(s, k, v, flags, workspace, str, &io)) != SOL_OK) return st;
   if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str, 0, &io)) != SOL_OK) return st;

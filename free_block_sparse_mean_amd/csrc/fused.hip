@@ -57,6 +57,7 @@
 #include <type_traits>
 
 #include "device_common.hpp"
+#include "queue_slots.hpp"
 #include "sol_internal.hpp"
 
 namespace sol {
@@ -95,12 +96,11 @@ struct FusedParams {
   int text_blocks;           // the last text_blocks blocks are text: always kept, dense rows
 };
 
-// Work-item queue counters, one per launch in flight (slots taken round-robin
-// by the host, each zeroed by queue_reset_kernel on the launch's stream just
-// before the launch): static device memory, nothing is allocated, and the
-// workspace stays read-only for the fused pass. Each translation unit that
-// holds fused kernels has its own pool.
-constexpr int kQueueSlots = 4096;
+// Work-item queue counters, one per launch in flight (slots handed out by the
+// host's QueueSlots pool, each zeroed by queue_reset_kernel on the launch's
+// stream just before the launch): static device memory, nothing is allocated,
+// and the workspace stays read-only for the fused pass. Each translation unit
+// that holds fused kernels has its own array.
 __device__ unsigned int kQueue[kQueueSlots];
 
 __global__ void queue_reset_kernel(int slot) {
@@ -1127,10 +1127,10 @@ const void* fused_row_reset_kernel() { return (const void*)queue_reset_kernel; }
 }  // namespace sol
 #else
 
-// Queue slot of the next launch: one counter for every fused launch of this
-// library (all instantiations, both translation units' pools), so that
-// launches in flight together never share a slot.
-std::atomic<unsigned> g_next_queue_slot{0};
+// Queue slots of every fused launch of this library (all instantiations, both
+// translation units' arrays), so that launches in flight together never share
+// a slot.
+QueueSlots g_queue_slots;
 
 template <typename T, int D>
 const void* kernel_for(const FusedArgs& a) {
@@ -1165,7 +1165,12 @@ hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
   p.text_blocks = a.text_blocks;
   p.dyn_heads = g.dyn_heads;
   p.n_static_wg = g.n_static_wg;
-  p.qslot = (int)(g_next_queue_slot.fetch_add(1u, std::memory_order_relaxed) % kQueueSlots);
+  // a launch recorded into a graph keeps its slot for every replay: it takes
+  // one from the range eager launches never use
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t ec = hipStreamIsCapturing(st, &cap);
+  if (ec != hipSuccess) return ec;
+  p.qslot = g_queue_slots.take(cap != hipStreamCaptureStatusNone);
   const dim3 grid((unsigned)(g.n_static_wg + g.workers));
   // this launch's queue counter, zeroed by a kernel of the fused kernel's own
   // translation unit (a kernel rather than a memset, so that the launch

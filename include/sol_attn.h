@@ -34,12 +34,19 @@
  * finished the work. Nothing here allocates device memory except
  * sol_attn_fwd, which keeps one library-owned workspace per device. The fused
  * pass deals part of its work from a counter in the library's static device
- * memory (16 KB per device), one of 4096 taken round-robin per launch: on
- * one stream any number of launches may be queued; across streams, at most
- * 4096 fused launches may be enqueued and not yet finished at a time. A fused
- * launch captured in a graph keeps its counter for every replay (the counter is
- * cleared by a kernel of the graph), so such a graph must not be replayed
- * concurrently with itself.
+ * memory (16 KB per device). Eager launches take one of 3072 counters
+ * round-robin: on one stream any number of launches may be queued; across
+ * streams, at most 3072 eager fused launches may be enqueued and not yet
+ * finished at a time. A fused launch recorded into a graph keeps its counter
+ * for every replay (the counter is cleared by a kernel of the graph); it takes
+ * one of the other 1024 counters, round-robin, which eager launches never use.
+ * So a graph must not be replayed concurrently with itself, nor with a graph
+ * captured 1024 fused launches earlier or later.
+ *
+ * Alignment: q, k, v and out must be 16-byte aligned device pointers, a
+ * caller workspace 256-byte aligned, and the optional int32 / float / uint64
+ * outputs aligned to their element size; a misaligned pointer gives
+ * SOL_ERR_INVALID_ARG.
  *
  * Errors: every entry point returns a sol_status and never aborts or throws.
  * Arguments are validated before any device call; on failure nothing has been
@@ -231,7 +238,13 @@ sol_status sol_route(const void* q, int B, int H, int N, int d, unsigned flags, 
                      int32_t* topk_idx, void* hip_stream);
 
 /* Whole forward on a caller stream with a caller workspace:
- * sol_block_summaries followed by sol_attn_fused. Reentrant. */
+ * sol_block_summaries followed by sol_attn_fused, i.e. the whole method of
+ * page "Sol-Attn: l'attenzione sparsa che sceglie al volo" (paithon.it):
+ * block summaries and closed-form thresholds (section "Una soglia per ogni
+ * riga"), then the one pass that routes, computes the kept blocks exactly and
+ * folds in the others (section "Scegliere mentre si calcola"); the paper
+ * abstract names the three parts of that pass. Reentrant: calls with
+ * distinct workspaces may run concurrently on different streams. */
 sol_status sol_attn_fwd_ex(const void* q, const void* k, const void* v, void* out,
                            int B, int H, int N, int d, float beta, unsigned flags,
                            void* hip_stream, void* workspace, size_t ws_bytes,
@@ -267,7 +280,13 @@ sol_status sol_attn_fwd_strided(const void* q, const void* k, const void* v, voi
 
 /* Whole forward on the null stream of the current device with a library-owned
  * workspace (allocated on first use, grown when needed, held until the
- * process ends; calls are serialised by a mutex). */
+ * process ends; calls are serialised by a mutex): the drop-in call of the
+ * agihunt.info page on the paper (closing paragraphs: a training-free kernel
+ * that replaces attention in an existing pipeline), computing what
+ * sol_attn_fwd_ex computes. The null stream does not order work against
+ * streams created non-blocking: a caller that produced q, k, v on such a
+ * stream must make the null stream wait for it (and its consumers wait for
+ * the null stream), or call sol_attn_fwd_ex on that stream. */
 sol_status sol_attn_fwd(const void* q, const void* k, const void* v, void* out,
                         int B, int H, int N, int d, float beta, unsigned flags);
 

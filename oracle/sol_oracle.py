@@ -284,23 +284,6 @@ def sol_attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: float,
             "tau": tau, "kept": mask.sum(axis=1)}
 
 
-def sol_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: float,
-                  correction: bool = True, route_dtype=np.float32) -> Dict[str, np.ndarray]:
-    """All heads: q, k, v [B, H, N, d]. Returns out [B, H, N, d] float64 and per-head routing."""
-    B, H, N, d = q.shape
-    nb = N // BLOCK
-    out = np.empty((B, H, N, d))
-    mask = np.empty((B, H, nb, nb), dtype=bool)
-    tau = np.empty((B, H, nb), dtype=route_dtype)
-    s_hat = np.empty((B, H, nb, nb), dtype=route_dtype)
-    for b in range(B):
-        for h in range(H):
-            r = sol_attention_head(q[b, h], k[b, h], v[b, h], beta, correction,
-                                   route_dtype=route_dtype)
-            out[b, h], mask[b, h], tau[b, h], s_hat[b, h] = r["out"], r["mask"], r["tau"], r["s_hat"]
-    return {"out": out, "mask": mask, "tau": tau, "s_hat": s_hat, "kept": mask.sum(axis=-1)}
-
-
 def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
     """Textbook softmax attention softmax(q k^T / sqrt(d)) v for one head, float64.
 

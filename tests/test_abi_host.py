@@ -150,3 +150,75 @@ def test_strided_validation(lib):
     assert call(sq=ref(sol_strides(N * H * d, d, 1 << 24))) == 1
     assert call(so=ref(sol_strides(N * H * d, d, 8))) == 1              # out rows would overlap
     assert "at least d" in lib.sol_last_error().decode()
+
+
+def test_misaligned_pointers_rejected(lib):
+    """Every entry point refuses q, k, v, out not 16-byte aligned, a workspace not
+    256-byte aligned and debug outputs not aligned to their elements, before any device
+    call (the pointers are never dereferenced)."""
+    p = ctypes.c_void_p(4096)
+    odd = ctypes.c_void_p(4096 + 8)
+    big = 1 << 30
+    B, H, N, d = 1, 1, 4096, 64
+
+    def expect(st, what):
+        assert st == 1, (what, st)
+        assert "aligned" in lib.sol_last_error().decode(), what
+
+    expect(lib.sol_attn_fwd(odd, p, p, p, B, H, N, d, 1.0, 0), "fwd q")
+    expect(lib.sol_attn_fwd(p, p, p, odd, B, H, N, d, 1.0, 0), "fwd out")
+    expect(lib.sol_attn_fwd_ex(p, odd, p, p, B, H, N, d, 1.0, 0, None, p, big, None), "fwd_ex k")
+    expect(lib.sol_attn_fwd_ex(p, p, p, p, B, H, N, d, 1.0, 0, None, ctypes.c_void_p(4096 + 16), big, None),
+           "fwd_ex workspace")
+    expect(lib.sol_block_summaries(p, odd, B, H, N, d, 0, p, big, None), "summaries v")
+    expect(lib.sol_block_summaries(p, p, B, H, N, d, 0, ctypes.c_void_p(4096 + 128), big, None),
+           "summaries workspace")
+    expect(lib.sol_attn_fused(p, p, odd, p, B, H, N, d, 1.0, 0, p, big, None, None), "fused v")
+    expect(lib.sol_attn_fused_joint(odd, p, p, p, B, H, N, d, 1.0, 0, 1, p, big, None, None), "joint q")
+    expect(lib.sol_attn_masked(p, p, p, odd, B, H, N, d, p, 0, p, big, None, None), "masked out")
+    expect(lib.sol_attn_masked(p, p, p, p, B, H, N, d, ctypes.c_void_p(4096 + 4), 0, p, big, None, None),
+           "masked mask_bits")
+    expect(lib.sol_route(odd, B, H, N, d, 0, 0, 1.0, 0, 0.0, p, big, p, p, None, None, None), "route q")
+    expect(lib.sol_route(p, B, H, N, d, 0, 0, 1.0, 0, 0.0, p, big, p, ctypes.c_void_p(4096 + 4), None, None,
+                         None), "route mask_bits")
+    from free_block_sparse_mean_amd.binding import sol_debug
+    dbg = sol_debug(None, ctypes.c_void_p(4096 + 4).value, None, None)
+    expect(lib.sol_attn_fused(p, p, p, p, B, H, N, d, 1.0, 0, p, big, ctypes.byref(dbg), None), "dbg mask_bits")
+    dbg = sol_debug(ctypes.c_void_p(4096 + 2).value, None, None, None)
+    expect(lib.sol_attn_fwd_ex(p, p, p, p, B, H, N, d, 1.0, 0, None, p, big, ctypes.byref(dbg)), "dbg kept")
+
+
+def test_queue_slot_pool(tmp_path):
+    """The pool of work-item queue counters (host C++, built here with g++): eager
+    launches never take a slot of the range kept for launches recorded into graphs,
+    and each range is dealt round-robin."""
+    src = tmp_path / "slots.cpp"
+    src.write_text(r'''
+#include <cstdio>
+#include "queue_slots.hpp"
+int main() {
+  sol::QueueSlots pool;
+  for (int i = 0; i < 3 * sol::kQueueSlots; ++i) {
+    const int e = pool.take(false);
+    if (e != i % sol::kEagerSlots) { std::printf("eager %d -> %d\n", i, e); return 1; }
+    if (i % 3 == 0) {
+      const int c = pool.take(true);
+      if (c < sol::kEagerSlots || c >= sol::kQueueSlots || c != sol::kEagerSlots + (i / 3) % sol::kCapturedSlots) {
+        std::printf("captured %d -> %d\n", i, c); return 1;
+      }
+    }
+  }
+  std::printf("ok\n");
+  return 0;
+}
+''')
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.fail("g++ is needed for this host test")
+    exe = tmp_path / "slots"
+    inc = os.path.join(ROOT, "free_block_sparse_mean_amd", "csrc")
+    subprocess.run([gxx, "-std=c++17", "-O1", "-I", inc, str(src), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr

@@ -33,9 +33,13 @@ def test_source_hash_ignores_comments_and_whitespace(tmp_path):
 
 
 def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch):
-    # the committed summary was taken from the current fused kernel source
-    t = bench.traffic_from_profile()
-    assert t is not None and t > 0
+    import json
+    summary = tmp_path / "pmc.json"
+    summary.write_text(json.dumps({"fused_src_sha256_16": bench.source_hash(bench.FUSED_SRC),
+                                   "hbm_bytes_per_launch": 123.0}))
+    monkeypatch.setattr(bench, "PMC_SUMMARY", str(summary))
+    # a summary taken from the current fused kernel source is reported
+    assert bench.traffic_from_profile() == 123.0
     changed = tmp_path / "fused.hip"
     changed.write_text(open(bench.FUSED_SRC, encoding="utf-8").read() + "\nint extra_symbol;\n")
     monkeypatch.setattr(bench, "FUSED_SRC", str(changed))

@@ -98,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sol_attn_fwd_ex.restype = i
     lib.sol_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, f, u]
     lib.sol_attn_fwd.restype = i
+    lib.sol_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, f, u, vp, ctypes.POINTER(sol_debug)]
+    lib.sol_attn_fwd_noalloc.restype = i
     sp = ctypes.POINTER(sol_strides)
     lib.sol_attn_fwd_strided.argtypes = [vp, vp, vp, vp, i, i, i, i, sp, sp, sp, sp, f, u, vp, vp, sz,
                                          ctypes.POINTER(sol_debug)]
@@ -319,6 +321,21 @@ def sol_attn_fwd_ex(q, k, v, out, beta: float, flags: int, stream=None,
                                           B, H, N, d, float(beta), flags, _stream(stream),
                                           workspace.data_ptr(), _ws_bytes(workspace),
                                           _dbg(kept_per_row, mask_bits, tau, item_clock)))
+
+
+def sol_attn_fwd_noalloc(q, k, v, out, beta: float, flags: int, stream=None, *, kept_per_row=None,
+                         mask_bits=None, tau=None, item_clock=None) -> None:
+    """sol_attn_fwd_ex without a workspace: the library's static per-GPU scratch (64 MiB)
+    holds the pre-pass arrays and nothing is allocated. Calls that may overlap on one GPU
+    race on that scratch."""
+    B, H, N, d = _shape(q)
+    _same_as(q, k=k, v=v, out=out)
+    _check_dbg(q, kept_per_row, mask_bits, tau, item_clock)
+    _dev(q, k, v, out)
+    flags |= _dtype_flag(q, k, v, out)
+    _check(load_library().sol_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                               B, H, N, d, float(beta), flags, _stream(stream),
+                                               _dbg(kept_per_row, mask_bits, tau, item_clock)))
 
 
 def _strides(t: torch.Tensor):

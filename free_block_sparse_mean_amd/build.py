@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsolattn.so")
-SOURCES = ["api.cpp", "prepass.hip", "fused.hip", "route.hip"]
+SOURCES = ["api.cpp", "prepass.hip", "fused.hip", "route.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -424,6 +424,27 @@ sol_status sol_attn_fwd_strided(const void* q, const void* k, const void* v, voi
   return finish(flags, str);
 }
 
+sol_status sol_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, int B, int H,
+                                int N, int d, float beta, unsigned flags, void* hip_stream,
+                                const sol_debug* dbg) {
+  sol::Shape s;
+  sol_status st = check_shape(B, H, N, d, &s);
+  if (st != SOL_OK) return st;
+  if ((st = check_fused_args(q, k, v, out, beta, flags)) != SOL_OK) return st;
+  if ((st = check_dbg_align(dbg)) != SOL_OK) return st;
+  const size_t need = sol::make_layout(s).total;
+  if (need > sol::kNoAllocScratchBytes)
+    return fail(SOL_ERR_UNSUPPORTED, "the shape needs %zu bytes of scratch, above the %zu-byte maximum of "
+                "sol_attn_fwd_noalloc (use sol_attn_fwd_ex with a workspace)", need, sol::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  hipError_t e = sol::noalloc_scratch(&ws);
+  if (e != hipSuccess) return device_fail(e, "scratch address lookup");
+  hipStream_t str = static_cast<hipStream_t>(hip_stream);
+  if ((st = summaries_checked(s, k, v, flags, ws, str)) != SOL_OK) return st;
+  if ((st = fused_checked(s, q, k, v, out, beta, flags, ws, dbg, str)) != SOL_OK) return st;
+  return finish(flags, str);
+}
+
 sol_status sol_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N,
                         int d, float beta, unsigned flags) {
   sol::Shape s;

@@ -124,5 +124,11 @@ const void* fused_row_kernel_bf16(int d);
 const void* fused_row_reset_kernel();
 hipError_t launch_route(const Shape& s, Dtype dt, const RouteArgs& a, hipStream_t stream);
 
+// Size of the static per-device scratch of sol_attn_fwd_noalloc (noalloc.hip).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+// Device address of that scratch on the current device (looked up on the
+// device's first call, then cached).
+hipError_t noalloc_scratch(void** out);
+
 
 }  // namespace sol

@@ -290,6 +290,22 @@ sol_status sol_attn_fwd_strided(const void* q, const void* k, const void* v, voi
 sol_status sol_attn_fwd(const void* q, const void* k, const void* v, void* out,
                         int B, int H, int N, int d, float beta, unsigned flags);
 
+/* For callers that cannot allocate device memory: code recorded into a HIP
+ * graph, tight serving loops, harnesses that forbid hipMalloc. The same
+ * forward as sol_attn_fwd_ex on a caller stream, with no caller workspace: the
+ * pre-pass arrays go to a scratch array of 64 MiB in the library's static
+ * device memory (one per GPU, held from library load until the process
+ * ends), and the call allocates and frees nothing. Shapes whose workspace
+ * (sol_attn_workspace_bytes) exceeds 64 MiB give SOL_ERR_UNSUPPORTED before
+ * any device work. Every call on one GPU uses that GPU's one scratch array,
+ * whose contents the previous call leaves behind (nothing in it has to start
+ * at zero): calls that may overlap on one GPU (on different streams, or a
+ * replayed graph and another call) race and must be ordered by the caller.
+ * Other arguments and errors as sol_attn_fwd_ex. */
+sol_status sol_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                                int B, int H, int N, int d, float beta, unsigned flags,
+                                void* hip_stream, const sol_debug* dbg);
+
 #ifdef __cplusplus
 }
 #endif

@@ -222,3 +222,17 @@ int main() {
     subprocess.run([gxx, "-std=c++17", "-O1", "-I", inc, str(src), "-o", str(exe)], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+def test_noalloc_rejects_beyond_its_scratch(lib):
+    """sol_attn_fwd_noalloc refuses, before any device call, a shape whose workspace
+    exceeds its 64 MiB scratch, and validates like sol_attn_fwd_ex."""
+    p = ctypes.c_void_p(4096)
+    B, H, N, d = 1, 24, 16384, 128
+    assert lib.sol_attn_workspace_bytes(B, H, N, d) > 64 * 2 ** 20
+    assert lib.sol_attn_fwd_noalloc(p, p, p, p, B, H, N, d, 1.0, 0, None, None) == 2
+    assert "64" in lib.sol_last_error().decode() and "sol_attn_fwd_ex" in lib.sol_last_error().decode()
+    assert lib.sol_attn_fwd_noalloc(None, p, p, p, 1, 1, 4096, 64, 1.0, 0, None, None) == 1
+    assert lib.sol_attn_fwd_noalloc(p, p, p, p, 1, 1, 4096, 64, math.nan, 0, None, None) == 1
+    assert lib.sol_attn_fwd_noalloc(p, p, p, p, 1, 1, 4096, 96, 1.0, 0, None, None) == 2
+    assert lib.sol_attn_fwd_noalloc(ctypes.c_void_p(4104), p, p, p, 1, 1, 4096, 64, 1.0, 0, None, None) == 1

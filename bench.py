@@ -121,62 +121,132 @@ def time_flushed(fn_pre, fn_fused, reps: int, flush=None):
 SWEEP_BETAS = {"c4_stress_128k": (1.2816, 1.5, 1.645, 2.0)}
 
 
-def sweep(names, reps: int) -> int:
-    """Per-config timing of every beta the configuration lists (with the correction, and
-    without it for the batched skewed config) and of the dense path: one JSON line per
-    configuration. Inputs smaller than twice the Infinity Cache are flushed before each
-    step by writing a 512 MiB buffer."""
+def dense_rows(qs, k, v):
+    """Textbook softmax attention of the query rows qs [r, d] over every key of one head,
+    float64 on the host (the reference of the error report)."""
+    import torch
+    qs, k, v = (torch.as_tensor(x, dtype=torch.float64) for x in (qs, k, v))
+    z = (qs @ k.T) / math.sqrt(qs.shape[1])
+    z = z - z.max(dim=1, keepdim=True).values
+    e = torch.exp(z)
+    return ((e @ v) / e.sum(dim=1, keepdim=True)).numpy()
+
+
+def config_sweep(name: str, reps: int, error_report: bool = False) -> dict:
+    """Timing of every beta a configuration lists (with the correction, and without it for
+    the batched skewed config) and of the dense path; inputs smaller than twice the
+    Infinity Cache are flushed before each step by writing a 512 MiB buffer. With
+    error_report: rel-L2 and max-abs of the output against dense attention on sampled rows
+    (two heads, four seeded query blocks each), for every beta with the per-row
+    correction, the block correction and none."""
+    import numpy as np
     import torch
     from free_block_sparse_mean_amd import binding as sb, workloads as wl
     dev = torch.device("cuda:0")
+    w = wl.CONFIGS[name]
+    t_gen = time.perf_counter()
+    q, k, v = wl.make_qkv(w)
+    t_gen = time.perf_counter() - t_gen
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(qd)
+    ws = sb.new_workspace(w.B, w.H, w.N, w.d, dev)
+    nb = w.n_blocks
+    kept = torch.zeros((w.B, w.H, nb), dtype=torch.int32, device=dev)
+    in_bytes = 3 * qd.numel() * qd.element_size()
+    flush = None
+    if in_bytes < 2 * 256 * 2 ** 20:
+        junk = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+        flush = lambda: junk.fill_(1)
+    pre = lambda: sb.sol_block_summaries(kd, vd, ws)
+
+    def one(beta, flags):
+        sb.sol_block_summaries(kd, vd, ws)
+        sb.sol_attn_fused(qd, kd, vd, out, beta, flags, ws, kept_per_row=kept)
+        torch.cuda.synchronize()
+        n_kept = int(kept.sum().item())
+        fused = lambda: sb.sol_attn_fused(qd, kd, vd, out, beta, flags, ws)
+        pre(); fused()
+        ms, fms, pms, each = time_flushed(pre, fused, reps, flush)
+        kf = kept_flop(w, n_kept)
+        return {"beta": beta if math.isfinite(beta) else str(beta),
+                "correction": bool(flags & (sb.SOL_CORRECTION | sb.SOL_CORRECTION_ROW)),
+                "ms": ms, "fused_ms": fms,
+                "prepass_ms": pms, "fused_ms_min": min(each),
+                "density": n_kept / (w.B * w.H * nb * nb),
+                "dense_equiv_tflops": dense_equiv_flop(w) / (ms * 1e-3) / 1e12,
+                "kept_tflops_fused": kf / (fms * 1e-3) / 1e12,
+                "mfma_frac_fused": kf / (fms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+    rows = []
+    betas = SWEEP_BETAS.get(name, w.betas)
+    corr_opts = (sb.SOL_CORRECTION, 0) if w.skewed else (sb.SOL_CORRECTION,)
+    for beta in betas:
+        for c in corr_opts:
+            rows.append(one(beta, c))
+    dense = one(-math.inf, sb.SOL_CORRECTION | sb.SOL_DENSE)
+    for r in rows:
+        r["speedup_vs_dense"] = dense["ms"] / r["ms"]
+    res = {"config": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "input_gen_s": t_gen,
+           "flushed": flush is not None, "reps": reps, "settings": rows, "dense": dense}
+    if error_report:
+        heads = [(0, 0), (w.B - 1, w.H - 1)]
+        rng = np.random.default_rng(5)
+        picks = {bh: np.sort(rng.choice(nb, size=4, replace=False)) for bh in heads}
+        idx = {bh: np.concatenate([np.arange(i * 64, (i + 1) * 64) for i in picks[bh]]) for bh in heads}
+        ref = np.concatenate([dense_rows(q[b, h][idx[(b, h)]].float().numpy(), k[b, h].float().numpy(),
+                                         v[b, h].float().numpy()) for (b, h) in heads])
+        table = []
+        for beta in w.betas:
+            row = {"beta": beta}
+            for tag, flags in (("row_correction", sb.SOL_CORRECTION_ROW), ("correction", sb.SOL_CORRECTION),
+                               ("none", 0)):
+                sb.sol_attn_fwd_ex(qd, kd, vd, out, beta, flags, workspace=ws, kept_per_row=kept)
+                torch.cuda.synchronize()
+                got = np.concatenate([out[b, h][torch.as_tensor(idx[(b, h)], device=dev)].float().cpu().numpy()
+                                      for (b, h) in heads])
+                row["density"] = int(kept.sum().item()) / (w.B * w.H * nb * nb)
+                row[tag] = {"rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref)),
+                            "max_abs": float(np.abs(got - ref).max())}
+            table.append(row)
+        res["error_vs_dense"] = {"rows": f"query blocks {', '.join(f'b{b}h{h}:{list(map(int, picks[(b, h)]))}' for (b, h) in heads)}",
+                                 "reference": "float64 softmax attention over every key (host)", "table": table}
+    del qd, kd, vd, out, ws, kept
+    torch.cuda.empty_cache()
+    return res
+
+
+def progress(msg: str) -> None:
+    """A progress line on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def sweep(names, reps: int) -> int:
+    """One JSON line per configuration (config_sweep)."""
     for name in names:
-        w = wl.CONFIGS[name]
-        q, k, v = wl.make_qkv(w)
-        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-        del q, k, v
-        out = torch.empty_like(qd)
-        ws = sb.new_workspace(w.B, w.H, w.N, w.d, dev)
-        nb = w.n_blocks
-        kept = torch.zeros((w.B, w.H, nb), dtype=torch.int32, device=dev)
-        in_bytes = 3 * qd.numel() * qd.element_size()
-        flush = None
-        if in_bytes < 2 * 256 * 2 ** 20:
-            junk = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
-            flush = lambda: junk.fill_(1)
-        pre = lambda: sb.sol_block_summaries(kd, vd, ws)
-
-        def one(beta, flags):
-            sb.sol_block_summaries(kd, vd, ws)
-            sb.sol_attn_fused(qd, kd, vd, out, beta, flags, ws, kept_per_row=kept)
-            torch.cuda.synchronize()
-            n_kept = int(kept.sum().item())
-            fused = lambda: sb.sol_attn_fused(qd, kd, vd, out, beta, flags, ws)
-            pre(); fused()
-            ms, fms, pms, each = time_flushed(pre, fused, reps, flush)
-            kf = kept_flop(w, n_kept)
-            return {"beta": beta if math.isfinite(beta) else str(beta),
-                    "correction": bool(flags & sb.SOL_CORRECTION), "ms": ms, "fused_ms": fms,
-                    "prepass_ms": pms, "fused_ms_min": min(each),
-                    "density": n_kept / (w.B * w.H * nb * nb),
-                    "dense_equiv_tflops": dense_equiv_flop(w) / (ms * 1e-3) / 1e12,
-                    "kept_tflops_fused": kf / (fms * 1e-3) / 1e12,
-                    "mfma_frac_fused": kf / (fms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-
-        rows = []
-        betas = SWEEP_BETAS.get(name, w.betas)
-        corr_opts = (sb.SOL_CORRECTION, 0) if w.skewed else (sb.SOL_CORRECTION,)
-        for beta in betas:
-            for c in corr_opts:
-                rows.append(one(beta, c))
-        dense = one(-math.inf, sb.SOL_CORRECTION | sb.SOL_DENSE)
-        for r in rows:
-            r["speedup_vs_dense"] = dense["ms"] / r["ms"]
-        print(json.dumps({"sweep": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                          "flushed": flush is not None, "reps": reps, "settings": rows,
-                          "dense": dense}), flush=True)
-        del qd, kd, vd, out, ws, kept
-        torch.cuda.empty_cache()
+        print(json.dumps(config_sweep(name, reps)), flush=True)
     return 0
+
+
+def calibrate_density(sb, qd, kd, vd, out, ws, w, kept, target: float, flags: int) -> float:
+    """beta at which the kernel's realised density is closest to `target`: bisection on the
+    kept counts of the fused pass (monotone in beta)."""
+    import torch
+    nb = w.n_blocks
+    lo, hi = 0.0, 4.0
+
+    def density(beta):
+        sb.sol_attn_fused(qd, kd, vd, out, beta, flags, ws, kept_per_row=kept)
+        torch.cuda.synchronize()
+        return int(kept.sum().item()) / (w.B * w.H * nb * nb)
+
+    sb.sol_block_summaries(kd, vd, ws)
+    for _ in range(14):
+        mid = 0.5 * (lo + hi)
+        if density(mid) > target:
+            lo = mid
+        else:
+            hi = mid
+    return lo if abs(density(lo) - target) <= abs(density(hi) - target) else hi
 
 
 def prepass_report(w, pre_ms: float) -> dict:
@@ -263,12 +333,15 @@ def load_balance(sb, qd, kd, vd, out, ws, beta, flags, w) -> dict:
 
 
 def routing_overhead(sb, qd, kd, vd, out, ws, beta, w, steps) -> dict:
-    """Kernel-time ablation at one beta on the same selection: the fused pass with and
-    without the correction against plain block-sparse attention on the routing's own
-    mask (sol_attn_masked: no routing, no correction). Pre-pass done beforehand, untimed."""
+    """Kernel-time ablation at one beta: the fused pass with and without the correction
+    against plain block-sparse attention on the routing's own mask (sol_attn_masked: no
+    routing, no correction), and the separate path the fused pass replaces: threshold
+    routing from a materialized proxy map (sol_route) followed by block-sparse attention
+    on that map's mask. Pre-pass done beforehand, untimed."""
     import torch
     nb = w.n_blocks
-    words = torch.zeros((w.B, w.H, nb, (nb + 63) // 64), dtype=torch.int64, device=qd.device)
+    W = (nb + 63) // 64
+    words = torch.zeros((w.B, w.H, nb, W), dtype=torch.int64, device=qd.device)
     sb.sol_block_summaries(kd, vd, ws)
     sb.sol_attn_fused(qd, kd, vd, out, beta, 0, ws, mask_bits=words)
     torch.cuda.synchronize()
@@ -287,9 +360,19 @@ def routing_overhead(sb, qd, kd, vd, out, ws, beta, w, steps) -> dict:
     masked = timed(lambda: sb.sol_attn_masked(qd, kd, vd, out, words, 0, ws))
     nocorr = timed(lambda: sb.sol_attn_fused(qd, kd, vd, out, beta, 0, ws))
     withcorr = timed(lambda: sb.sol_attn_fused(qd, kd, vd, out, beta, sb.SOL_CORRECTION, ws))
+    pm = torch.empty((w.B, w.H, nb, nb), dtype=torch.float32, device=qd.device)
+    map_words = torch.zeros_like(words)
+    route = timed(lambda: sb.sol_route(qd, sb.SOL_ROUTE_THRESHOLD, ws, pm, map_words, beta=beta))
+    masked_map = timed(lambda: sb.sol_attn_masked(qd, kd, vd, out, map_words, 0, ws))
+    same = int((map_words != words).sum().item())
+    del pm
     return {"beta": beta, "reps": steps, "given_mask_ms": masked, "fused_no_correction_ms": nocorr,
             "fused_ms": withcorr, "routing_overhead": nocorr / masked - 1.0,
-            "routing_and_correction_overhead": withcorr / masked - 1.0}
+            "routing_and_correction_overhead": withcorr / masked - 1.0,
+            "separate_path": {"map_routing_ms": route, "block_sparse_on_map_mask_ms": masked_map,
+                              "total_ms": route + masked_map, "mask_words_differing_from_fused": same},
+            "fused_vs_separate": withcorr / (route + masked_map),
+            "fused_no_correction_vs_separate": nocorr / (route + masked_map)}
 
 
 def routing_study(sb, qd, kd, vd, out, ws, w, steps) -> dict:
@@ -367,9 +450,12 @@ def main() -> int:
     ap.add_argument("--no-correction", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-routing-study", action="store_true")
-    ap.add_argument("--cpu-blocks-per-head", type=int, default=24)
+    ap.add_argument("--cpu-blocks-per-head", type=int, default=96)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (for counter scaling)")
+    ap.add_argument("--configs", default="c2_video_16k,c3_dit14b_77k,c5_batched_skewed_64k",
+                    help="other configurations timed in the default run ('' for none)")
+    ap.add_argument("--config-reps", type=int, default=5)
     ap.add_argument("--sweep", default="",
                     help="comma list of bf16 configs to time at every beta they list (one JSON "
                          "line each) instead of the headline benchmark")
@@ -442,6 +528,7 @@ def main() -> int:
         }
 
     head = measure(args.beta, corr, args.steps, args.warmup)
+    progress(f"headline beta {args.beta}: {head['ms']:.3f} ms per step")
     # the two-call step equals one sol_attn_fwd_ex call (bit for bit)
     ref = out.clone()
     sb.sol_attn_fwd_ex(qd, kd, vd, out, args.beta, corr, workspace=ws)
@@ -452,11 +539,21 @@ def main() -> int:
     ablation = routing_overhead(sb, qd, kd, vd, out, ws, args.beta, w, max(3, args.steps // 2))
     rowc = None if args.no_correction else measure(args.beta, sb.SOL_CORRECTION_ROW, max(3, args.steps // 2), 1)
     study = None if args.no_routing_study else routing_study(sb, qd, kd, vd, out, ws, w, 5)
+    if study is not None:
+        # like for like: the in-pass routing's cost inside the fused pass (fused pass without
+        # the correction minus plain block-sparse attention on the same selection) against
+        # routing from a materialized map; and the whole paths
+        study["in_pass_routing_in_context_ms"] = ablation["fused_no_correction_ms"] - ablation["given_mask_ms"]
+        study["map_routing_at_headline_beta_ms"] = ablation["separate_path"]["map_routing_ms"]
+    progress("ablation, per-row correction and routing study done")
 
     per_beta = {str(args.beta): head}
     small_steps = max(3, args.steps // 2)
     for b in [float(x) for x in args.extra_betas.split(",") if x.strip()]:
         per_beta[str(b)] = measure(b, corr, small_steps, 1)
+    calib = calibrate_density(sb, qd, kd, vd, out, ws, w, kept, 0.05, corr)
+    per_beta["5pct"] = measure(calib, corr, small_steps, 1)
+    per_beta["5pct"]["calibrated_for_density"] = 0.05
     if not args.no_dense:
         dense = measure(-math.inf, corr | sb.SOL_DENSE, small_steps, 1)
         per_beta["dense"] = dense
@@ -471,6 +568,14 @@ def main() -> int:
                 "traffic": traffic_from_profile(),
                 "kernel": "fused_kernel<bf16,128,correction>",
                 "algorithmic_flop_per_launch": kf}
+
+    # the other configurations (each generated, timed and freed in turn)
+    del qd, kd, vd, out, ws
+    torch.cuda.empty_cache()
+    configs = {}
+    for name in [x for x in args.configs.split(",") if x]:
+        configs[name] = config_sweep(name, args.config_reps, error_report=wl.CONFIGS[name].skewed)
+        progress(f"config {name} done")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -502,6 +607,7 @@ def main() -> int:
         "row_correction": rowc,
         "routing_study": study,
         "prepass": prepass_report(w, head["prepass_ms"]),
+        "configs": configs,
         "checks": {"two_call_step_equals_fwd_ex": same_as_fwd_ex},
         "input_gen_s": t_gen,
         "device": torch.cuda.get_device_name(0),

@@ -450,6 +450,8 @@ def main() -> int:
     ap.add_argument("--no-correction", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-routing-study", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the beta calibrated to 5%% density (it runs the fused pass at many betas)")
     ap.add_argument("--cpu-blocks-per-head", type=int, default=96)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (for counter scaling)")
@@ -551,9 +553,10 @@ def main() -> int:
     small_steps = max(3, args.steps // 2)
     for b in [float(x) for x in args.extra_betas.split(",") if x.strip()]:
         per_beta[str(b)] = measure(b, corr, small_steps, 1)
-    calib = calibrate_density(sb, qd, kd, vd, out, ws, w, kept, 0.05, corr)
-    per_beta["5pct"] = measure(calib, corr, small_steps, 1)
-    per_beta["5pct"]["calibrated_for_density"] = 0.05
+    if not args.no_calibration:
+        calib = calibrate_density(sb, qd, kd, vd, out, ws, w, kept, 0.05, corr)
+        per_beta["5pct"] = measure(calib, corr, small_steps, 1)
+        per_beta["5pct"]["calibrated_for_density"] = 0.05
     if not args.no_dense:
         dense = measure(-math.inf, corr | sb.SOL_DENSE, small_steps, 1)
         per_beta["dense"] = dense

@@ -93,7 +93,13 @@ sol_status check_shape(int B, int H, int N, int d, sol::Shape* s) {
   s->n_b = N / sol::kBlock;
   s->n_b_pad = (s->n_b + 3) & ~3;
   s->n_words = (s->n_b + 63) / 64;
-  s->cov_parts = (s->n_b + sol::kCovChunk - 1) / sol::kCovChunk;
+  // partials of 128 key blocks, halved (down to 32) while the moment kernel
+  // would get fewer than 512 workgroups; this keeps B*H*cov_parts <= 512
+  // whenever the chunk shrinks, so the partials stay bounded
+  s->cov_chunk = sol::kCovChunk;
+  while (s->cov_chunk > 32 && 2LL * B * H * ((s->n_b + s->cov_chunk - 1) / s->cov_chunk) < 512)
+    s->cov_chunk /= 2;
+  s->cov_parts = (s->n_b + s->cov_chunk - 1) / s->cov_chunk;
   if ((long long)B * H * s->n_b > 0x7fffffffLL)
     return fail(SOL_ERR_UNSUPPORTED, "B*H*N/64 exceeds the launch grid limit");
   return SOL_OK;

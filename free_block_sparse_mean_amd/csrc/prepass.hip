@@ -138,7 +138,8 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const T* __restrict__ k
 }
 
 // Partial first and second moments of the key summaries over one chunk of
-// kCovChunk blocks, in double; also writes the transposed summaries kbar_t.
+// `chunk` blocks (a multiple of 32), in double; also writes the transposed
+// summaries kbar_t.
 // blockIdx.z picks half of the D x D partial (rows z*D/2 ..); thread (ty, tx)
 // holds rows z*D/2 + ty + 16r and columns tx + 16s, so the 16 threads of a
 // row group read 16 consecutive doubles of a staged summary (no bank
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(256) void moments_partial_kernel(const float* __res
                                                               float* __restrict__ kbar_t,
                                                               double* __restrict__ s1_part,
                                                               double* __restrict__ s2_part,
-                                                              int n_b, int n_b_pad, int parts) {
+                                                              int n_b, int n_b_pad, int parts, int chunk) {
   constexpr int TJ = 32;            // key blocks staged per step
   constexpr int RR = D / 32;        // rows per thread (half of the D rows over 16 row groups)
   constexpr int RC = D / 16;        // columns per thread
@@ -157,8 +158,8 @@ __global__ __launch_bounds__(256) void moments_partial_kernel(const float* __res
   const int t = threadIdx.x, ty = t / 16, tx = t % 16;
   const long long bh = blockIdx.y;
   const int part = blockIdx.x, z = blockIdx.z;
-  const int j0 = part * kCovChunk;
-  const int j1 = min(n_b, j0 + kCovChunk);
+  const int j0 = part * chunk;
+  const int j1 = min(n_b, j0 + chunk);
   const int r0 = z * (D / 2);
   double acc[RR][RC];
   double s1 = 0.0;
@@ -238,22 +239,24 @@ __global__ __launch_bounds__(256) void moments_reduce_kernel(const double* __res
 // Block summaries as bf16 MFMA tiles, for the per-row correction: chunk c of
 // 64 key blocks gives a K-like tile [64][D] of k_bar_j and a V^T-like tile
 // [D][64] of v_bar_j = vsum_j / 64 in the column order of the V^T tiles; rows
-// and columns past n_b are zero (the fused pass masks them out).
+// and columns past n_b are zero (the fused pass masks them out). blockIdx.z
+// takes a quarter of the head dims.
 template <int D>
 __global__ __launch_bounds__(256) void virtual_tiles_kernel(const float* __restrict__ kbar,
                                                             const float* __restrict__ vsum,
                                                             __bf16* __restrict__ kbar_bf,
                                                             __bf16* __restrict__ vbar_t, int n_b,
                                                             int n_chunks) {
-  const int c = blockIdx.x, t = threadIdx.x;
+  constexpr int DQ = D / 4;   // head dims of this workgroup
+  const int c = blockIdx.x, t = threadIdx.x, d0 = blockIdx.z * DQ;
   const long long bh = blockIdx.y;
   __bf16* kd = kbar_bf + ((size_t)bh * n_chunks + c) * 64 * D;
-  for (int e = t; e < 64 * D; e += 256) {
-    const int r = e / D, dd = e % D, j = 64 * c + r;
-    kd[e] = j < n_b ? to_bf16(kbar[((size_t)bh * n_b + j) * D + dd]) : to_bf16(0.f);
+  for (int e = t; e < 64 * DQ; e += 256) {
+    const int r = e / DQ, dd = d0 + e % DQ, j = 64 * c + r;
+    kd[r * D + dd] = j < n_b ? to_bf16(kbar[((size_t)bh * n_b + j) * D + dd]) : to_bf16(0.f);
   }
   __bf16* vd = vbar_t + ((size_t)bh * n_chunks + c) * D * 64;
-  for (int e = t; e < D * 64; e += 256) {
+  for (int e = d0 * 64 + t; e < (d0 + DQ) * 64; e += 256) {
     const int dd = e / 64, col = e % 64, kc = col / 8, ee = col % 8;
     const int j = 64 * c + 32 * (kc >> 2) + 4 * (kc & 3) + 16 * (ee >> 2) + (ee & 3);
     vd[e] = j < n_b ? to_bf16(vsum[((size_t)bh * n_b + j) * D + dd] * (1.0f / kBlock)) : to_bf16(0.f);
@@ -271,10 +274,10 @@ hipError_t prepass_impl(const Shape& s, const void* k, const void* v, const TStr
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((moments_partial_kernel<D>), dim3(s.cov_parts, bh, 2), dim3(256), 0, st, ws.kbar,
-                     ws.kbar_t, ws.s1_part, ws.s2_part, s.n_b, s.n_b_pad, s.cov_parts);
+                     ws.kbar_t, ws.s1_part, ws.s2_part, s.n_b, s.n_b_pad, s.cov_parts, s.cov_chunk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if constexpr (kVT) {
-    hipLaunchKernelGGL((virtual_tiles_kernel<D>), dim3(s.n_words, bh), dim3(256), 0, st, ws.kbar, ws.vsum,
+    hipLaunchKernelGGL((virtual_tiles_kernel<D>), dim3(s.n_words, bh, 4), dim3(256), 0, st, ws.kbar, ws.vsum,
                        ws.kbar_bf, ws.vbar_t, s.n_b, s.n_words);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -10,7 +10,7 @@ namespace sol {
 
 constexpr int kBlock = 64;          // tokens per block
 constexpr int kMaxBlocks = 4096;    // n_b limit (N <= 262144), bounded by the fused kernel's LDS
-constexpr int kCovChunk = 128;      // key blocks per covariance partial
+constexpr int kCovChunk = 128;      // key blocks per covariance partial (halved to 32 for small problems)
 
 enum class Dtype { BF16, F32 };
 
@@ -22,7 +22,8 @@ struct Shape {
   int n_b;      // N / 64
   int n_b_pad;  // n_b rounded up to a multiple of 4 (row pitch of kbar_t)
   int n_words;  // ceil(n_b / 64): mask words per query block
-  int cov_parts;  // ceil(n_b / kCovChunk)
+  int cov_chunk;  // key blocks per covariance partial: kCovChunk, 64 or 32 (small problems)
+  int cov_parts;  // ceil(n_b / cov_chunk)
   long long BH() const { return (long long)B * H; }
 };
 

@@ -198,7 +198,12 @@ def test_graph_capture_replays(gpu_lib):
         assert torch.equal(out, ref), f"replay {rep}"
 
 
-@pytest.mark.parametrize("w", [SMALL[0], SMALL[1], SMALL[2]], ids=lambda w: w.name)
+# The moment kernels sum key-block chunks of 128, 64 or 32 blocks (smaller when B*H*n_b is
+# small): the small cases take chunks of 32 (several per head), this one chunks of 64.
+CHUNK64 = wl.small("chunk64_d64", 1, 16, 65536, 64, grid=(16, 64, 64))
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[1], SMALL[2], CHUNK64], ids=lambda w: w.name)
 def test_prepass_summaries(w, gpu_lib):
     """k_bar, v sums, m and C of the pre-pass against the oracle's float64 block means."""
     from oracle import sol_oracle as orc

@@ -648,25 +648,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     using V16 = Vec16<T>;
     constexpr int E = V16::kN, CH = D / E, RPT = 64 * CH / 256, RSTEP = 256 / CH;
     const int cc = t % CH, r0 = t / CH;
-    for (int g = 0; g < nG; ++g) {
-      const T* Qb = Qh + (long long)(qi0 + g) * kBlock * p.qs.n;
-      float s[E];
+    // every block's loads first (one round of L2/HBM latency for the group)
+    typename V16::raw rq[kGMax][RPT];
 #pragma unroll
-      for (int e = 0; e < E; ++e) s[e] = 0.f;
+    for (int g = 0; g < kGMax; ++g) {
+      if (g < nG) {
+        const T* Qb = Qh + (long long)(qi0 + g) * kBlock * p.qs.n;
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        float f[E];
-        V16::to_float(reinterpret_cast<const typename V16::raw*>(Qb + (long long)(r0 + RSTEP * i) * p.qs.n)[cc], f);
-#pragma unroll
-        for (int e = 0; e < E; ++e) s[e] += f[e];
+        for (int i = 0; i < RPT; ++i)
+          rq[g][i] = reinterpret_cast<const typename V16::raw*>(Qb + (long long)(r0 + RSTEP * i) * p.qs.n)[cc];
       }
+    }
 #pragma unroll
-      for (int o = CH; o < 64; o <<= 1)
+    for (int g = 0; g < kGMax; ++g) {
+      if (g < nG) {
+        float s[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) s[e] += __shfl_xor(s[e], o, 64);
-      if (lane < CH)
+        for (int e = 0; e < E; ++e) s[e] = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[(w * kGMax + g) * D + cc * E + e] = s[e];
+        for (int i = 0; i < RPT; ++i) {
+          float f[E];
+          V16::to_float(rq[g][i], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) s[e] += f[e];
+        }
+#pragma unroll
+        for (int o = CH; o < 64; o <<= 1)
+#pragma unroll
+          for (int e = 0; e < E; ++e) s[e] += __shfl_xor(s[e], o, 64);
+        if (lane < CH)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[(w * kGMax + g) * D + cc * E + e] = s[e];
+      }
     }
   }
   __syncthreads();
@@ -686,19 +699,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   {
     const float* C = p.kcov + (size_t)bh * D * D;
     const float* m = p.kmean + (size_t)bh * D;
-    constexpr int P = 256 / D;
-    const int r = t % D, part = t / D;
-    float y[kGMax] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 16
-    for (int c = part; c < D; c += P) {
-      const float cv = C[(size_t)c * D + r];
-      const float4 qv = *reinterpret_cast<const float4*>(qa + c * kGMax);
-      y[0] += cv * qv.x; y[1] += cv * qv.y; y[2] += cv * qv.z; y[3] += cv * qv.w;
+    // thread (part, r4): rows r4 .. r4+3 of C q_bar over CP consecutive c,
+    // one float4 of C per c, all CP loads in flight at once
+    constexpr int RQ = D / 4, NP = 256 / RQ, CP = D / NP;
+    const int r4 = 4 * (t % RQ), part = t / RQ;
+    float4 cv[CP];
+#pragma unroll
+    for (int i = 0; i < CP; ++i) cv[i] = *reinterpret_cast<const float4*>(C + (size_t)(part * CP + i) * D + r4);
+    float y[kGMax][4];
+#pragma unroll
+    for (int g = 0; g < kGMax; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[g][e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CP; ++i) {
+      const float4 qv = *reinterpret_cast<const float4*>(qa + (part * CP + i) * kGMax);
+      const float qg[4] = {qv.x, qv.y, qv.z, qv.w};
+      const float cr[4] = {cv[i].x, cv[i].y, cv[i].z, cv[i].w};
+#pragma unroll
+      for (int g = 0; g < kGMax; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[g][e] += cr[e] * qg[g];
     }
-    const float4 qr = *reinterpret_cast<const float4*>(qa + r * kGMax);
-    const float mr = part == 0 ? m[r] : 0.f;
-    float v8[8] = {qr.x * y[0], qr.y * y[1], qr.z * y[2], qr.w * y[3],
-                   qr.x * mr, qr.y * mr, qr.z * mr, qr.w * mr};
+    const float4 mv = part == 0 ? *reinterpret_cast<const float4*>(m + r4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float mr[4] = {mv.x, mv.y, mv.z, mv.w};
+    float v8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float4 qr = *reinterpret_cast<const float4*>(qa + (r4 + e) * kGMax);
+      const float qe[4] = {qr.x, qr.y, qr.z, qr.w};
+#pragma unroll
+      for (int g = 0; g < kGMax; ++g) {
+        v8[g] += qe[g] * y[g][e];
+        v8[4 + g] += qe[g] * mr[e];
+      }
+    }
     block_sum_n<8>(v8, misc);
     if (t < nG) {
       const float qcq = misc[kTot + t], qm = misc[kTot + 4 + t];
@@ -840,7 +875,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       const bf16x8 zero8 = {};
-      for (int ks = w; ks < 2 * n_words; ks += 4) {
+      // k-steps of 32 key blocks, four per wave at a time: the L2 loads of
+      // their v_bar^T operands are all issued before the first MFMA
+      const int nks = 2 * n_words;
+      int ks = w;
+      for (; ks + 12 < nks; ks += 16) {
+        bf16x8 av[4][D / 16], bw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int k1 = ks + 4 * u;
+          const __bf16* vrow = vbt + ((size_t)(k1 >> 1) * D + l16) * 64 + 32 * (k1 & 1) + 8 * grp;
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt)
+            av[u][dt] = *reinterpret_cast<const bf16x8*>(vrow + (size_t)dt * 16 * 64);
+          bw[u] = l16 < nG ? *reinterpret_cast<const bf16x8*>(wrow(l16 < 4 ? l16 : 0) + 32 * k1 + 8 * grp)
+                           : zero8;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u][dt], bw[u], o[dt], 0, 0, 0);
+      }
+      for (; ks < nks; ks += 4) {
         const bf16x8 bw = l16 < nG ? *reinterpret_cast<const bf16x8*>(wrow(l16 < 4 ? l16 : 0) + 32 * ks + 8 * grp)
                                    : zero8;
         const __bf16* vrow = vbt + ((size_t)(ks >> 1) * D + l16) * 64 + 32 * (ks & 1) + 8 * grp;

@@ -55,58 +55,83 @@ __global__ __launch_bounds__(256) void qbar_kernel(const T* __restrict__ q, floa
 }
 
 // map[bh][i][j] = (sum_c qbar[i][c] kbar[j][c]) / sqrt(d), dims summed in
-// ascending order. A workgroup computes 64 x 64 entries, 4 x 4 per lane, from
-// LDS copies of the two 64 x D tiles (odd row pitch: the 16 column groups of a
-// wave read 16 distinct banks).
+// ascending order (one fp32 FMA chain per entry). A workgroup computes a
+// 128 x 128 tile, 8 x 8 entries per lane (rows 8ty.., columns 8tx..), from
+// chunks of 16 head dims of both operands staged in LDS transposed ([c][128],
+// so a lane's eight rows or columns are two 16-byte reads); 64 FMAs per four
+// LDS reads. Rows and columns past n_b are computed on zeros and not stored.
 template <int D>
 __global__ __launch_bounds__(256) void proxy_map_kernel(const float* __restrict__ qbar,
                                                         const float* __restrict__ kbar,
                                                         float* __restrict__ map, int n_b) {
-  constexpr int P = D + 1;
-  __shared__ float qs[64 * P];
-  __shared__ float ks[64 * P];
+  constexpr int TC = 16;          // head dims per staged chunk
+  constexpr int PT = 128 + 4;     // pitch of a staged row of 128 entries
+  __shared__ __attribute__((aligned(16))) float qs[TC * PT];
+  __shared__ __attribute__((aligned(16))) float ks[TC * PT];
   const long long bh = blockIdx.z;
-  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64, t = threadIdx.x;
+  const int i0 = blockIdx.y * 128, j0 = blockIdx.x * 128, t = threadIdx.x;
   const float* qb = qbar + (size_t)bh * n_b * D;
   const float* kb = kbar + (size_t)bh * n_b * D;
-  for (int e = t; e < 64 * (D / 4); e += 256) {
-    const int r = e / (D / 4), c4 = e % (D / 4);
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
-    if (i0 + r < n_b) x = reinterpret_cast<const float4*>(qb + (size_t)(i0 + r) * D)[c4];
-    if (j0 + r < n_b) y = reinterpret_cast<const float4*>(kb + (size_t)(j0 + r) * D)[c4];
-    float* qd = qs + r * P + 4 * c4;
-    float* kd = ks + r * P + 4 * c4;
-    qd[0] = x.x; qd[1] = x.y; qd[2] = x.z; qd[3] = x.w;
-    kd[0] = y.x; kd[1] = y.y; kd[2] = y.z; kd[3] = y.w;
-  }
-  __syncthreads();
   const int ty = t / 16, tx = t % 16;
-  float acc[4][4];
+  float acc[8][8];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
-  for (int c = 0; c < D; ++c) {
-    float qv[4], kv[4];
+    for (int b = 0; b < 8; ++b) acc[a][b] = 0.f;
+  // staging: lane t loads float4 (row t / 4 + 64 h, dims 4 (t % 4) ..) of both operands
+  const int sr = t / 4, sc = 4 * (t % 4);
+  for (int c0 = 0; c0 < D; c0 += TC) {
+    float4 x[2], y[2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) qv[a] = qs[(ty * 4 + a) * P + c];
+    for (int h = 0; h < 2; ++h) {
+      const int r = sr + 64 * h;
+      x[h] = i0 + r < n_b ? *reinterpret_cast<const float4*>(qb + (size_t)(i0 + r) * D + c0 + sc)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      y[h] = j0 + r < n_b ? *reinterpret_cast<const float4*>(kb + (size_t)(j0 + r) * D + c0 + sc)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();   // the previous chunk has been read
 #pragma unroll
-    for (int b = 0; b < 4; ++b) kv[b] = ks[(tx * 4 + b) * P + c];
+    for (int h = 0; h < 2; ++h) {
+      const int r = sr + 64 * h;
+      qs[(sc + 0) * PT + r] = x[h].x; qs[(sc + 1) * PT + r] = x[h].y;
+      qs[(sc + 2) * PT + r] = x[h].z; qs[(sc + 3) * PT + r] = x[h].w;
+      ks[(sc + 0) * PT + r] = y[h].x; ks[(sc + 1) * PT + r] = y[h].y;
+      ks[(sc + 2) * PT + r] = y[h].z; ks[(sc + 3) * PT + r] = y[h].w;
+    }
+    __syncthreads();
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int c = 0; c < TC; ++c) {
+      const float4 q0 = *reinterpret_cast<const float4*>(qs + c * PT + 8 * ty);
+      const float4 q1 = *reinterpret_cast<const float4*>(qs + c * PT + 8 * ty + 4);
+      const float4 k0 = *reinterpret_cast<const float4*>(ks + c * PT + 8 * tx);
+      const float4 k1 = *reinterpret_cast<const float4*>(ks + c * PT + 8 * tx + 4);
+      const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(qv[a], kv[b], acc[a][b]);
+      for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) acc[a][b] = fmaf(qv[a], kv[b], acc[a][b]);
+    }
   }
   const float scale = D == 64 ? 0.125f : 0.08838834764831845f;
+  const int j = j0 + 8 * tx;
+  // 16-byte stores where every row starts 16-byte aligned
+  const bool vec = (n_b & 3) == 0 && (reinterpret_cast<uintptr_t>(map) & 15) == 0;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + ty * 4 + a;
+  for (int a = 0; a < 8; ++a) {
+    const int i = i0 + 8 * ty + a;
     if (i >= n_b) continue;
     float* row = map + ((size_t)bh * n_b + i) * n_b;
+    if (vec && j + 8 <= n_b) {
+      *reinterpret_cast<float4*>(row + j) =
+          make_float4(acc[a][0] * scale, acc[a][1] * scale, acc[a][2] * scale, acc[a][3] * scale);
+      *reinterpret_cast<float4*>(row + j + 4) =
+          make_float4(acc[a][4] * scale, acc[a][5] * scale, acc[a][6] * scale, acc[a][7] * scale);
+    } else {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = j0 + tx * 4 + b;
-      if (j < n_b) row[j] = acc[a][b] * scale;
+      for (int b = 0; b < 8; ++b)
+        if (j + b < n_b) row[j + b] = acc[a][b] * scale;
     }
   }
 }
@@ -145,21 +170,38 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
   int n_kept = 0;
 
   if constexpr (MODE == kRouteThreshold) {
-    // mu and sigma of the materialized row (two passes), tau, strict test
+    // the row is read once into registers: lane t holds entries t + 256 k,
+    // which are also the entries it tests for mask word 4 k + (its wave);
+    // mu and sigma of the materialized row (two passes over the registers),
+    // tau, strict test
+    constexpr int C = kMaxBlocks / 256;
+    float xv[C];
     float s = 0.f;
-    for (int j = t; j < n_b; j += 256) s += x[j];
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+      const int j = t + 256 * k;
+      xv[k] = j < n_b ? x[j] : 0.f;
+      s += xv[k];
+    }
     const float mu = wg_sum(s, red) / (float)n_b;
     float v = 0.f;
-    for (int j = t; j < n_b; j += 256) { const float e = x[j] - mu; v = fmaf(e, e, v); }
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+      const float e = xv[k] - mu;
+      if (t + 256 * k < n_b) v = fmaf(e, e, v);
+    }
     const float sigma = sqrtf(wg_sum(v, red + 4) / (float)n_b);
     const float tau = beta_mode == kBetaMinusInf ? -INFINITY
                       : beta_mode == kBetaPlusInf ? INFINITY
                                                   : mu + beta * sigma;
-    for (int wi = w; wi < n_words; wi += 4) {
-      const int j = wi * 64 + lane;
-      const uint64_t word = __ballot(j < n_b && x[j] > tau);
-      if (lane == 0) mask[(size_t)row * n_words + wi] = word;
-      n_kept += (lane == 0) ? __popcll(word) : 0;
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+      const int wi = 4 * k + w, j = wi * 64 + lane;   // = t + 256 k
+      if (wi < n_words) {                             // uniform over the wave
+        const uint64_t word = __ballot(j < n_b && xv[k] > tau);
+        if (lane == 0) mask[(size_t)row * n_words + wi] = word;
+        n_kept += (lane == 0) ? __popcll(word) : 0;
+      }
     }
     n_kept = (int)wg_sum((float)n_kept, red);
   } else {
@@ -242,7 +284,7 @@ hipError_t route_impl(const Shape& s, const RouteArgs& a, hipStream_t st) {
                      static_cast<const T*>(a.q), a.ws.qbar, s.n_b, s.H, a.qs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned tiles = (unsigned)((s.n_b + 63) / 64);
+  const unsigned tiles = (unsigned)((s.n_b + 127) / 128);
   hipLaunchKernelGGL((proxy_map_kernel<D>), dim3(tiles, tiles, bh), dim3(256), 0, st, a.ws.qbar,
                      a.ws.kbar, a.proxy_map, s.n_b);
   if ((e = hipGetLastError()) != hipSuccess) return e;

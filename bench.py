@@ -539,7 +539,7 @@ def main() -> int:
     rows = row_stats(kept)
     balance = load_balance(sb, qd, kd, vd, out, ws, args.beta, corr, w)
     ablation = routing_overhead(sb, qd, kd, vd, out, ws, args.beta, w, max(3, args.steps // 2))
-    rowc = None if args.no_correction else measure(args.beta, sb.SOL_CORRECTION_ROW, max(3, args.steps // 2), 1)
+    rowc = None if args.no_correction else measure(args.beta, sb.SOL_CORRECTION_ROW, max(3, args.steps // 2), 3)
     study = None if args.no_routing_study else routing_study(sb, qd, kd, vd, out, ws, w, 5)
     if study is not None:
         # like for like: the in-pass routing's cost inside the fused pass (fused pass without
@@ -552,13 +552,13 @@ def main() -> int:
     per_beta = {str(args.beta): head}
     small_steps = max(3, args.steps // 2)
     for b in [float(x) for x in args.extra_betas.split(",") if x.strip()]:
-        per_beta[str(b)] = measure(b, corr, small_steps, 1)
+        per_beta[str(b)] = measure(b, corr, small_steps, 3)
     if not args.no_calibration:
         calib = calibrate_density(sb, qd, kd, vd, out, ws, w, kept, 0.05, corr)
-        per_beta["5pct"] = measure(calib, corr, small_steps, 1)
+        per_beta["5pct"] = measure(calib, corr, small_steps, 3)
         per_beta["5pct"]["calibrated_for_density"] = 0.05
     if not args.no_dense:
-        dense = measure(-math.inf, corr | sb.SOL_DENSE, small_steps, 1)
+        dense = measure(-math.inf, corr | sb.SOL_DENSE, small_steps, 3)
         per_beta["dense"] = dense
         for key, r in per_beta.items():
             if key != "dense":

@@ -135,3 +135,26 @@ def test_topk_masks_drive_block_sparse_attention(gpu_lib):
                                          mask_override=mask[b, h])["out"]
             assert pu.rel_l2(got[b, h], ref) <= pu.BF16_REL_L2
             assert float(np.abs(got[b, h] - ref).max()) <= pu.BF16_MAX_ABS
+
+
+@pytest.mark.parametrize("w", [CASES[1], CASES[3]], ids=lambda w: w.name)
+def test_proxy_map_unaligned_output(w, gpu_lib):
+    """A proxy map that starts 4 bytes past a 16-byte boundary takes the map kernel's
+    element-wise stores instead of its 16-byte ones: the same map and masks, bit for bit."""
+    q, k, v = wl.make_qkv(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    nb = w.n_blocks
+    W = (nb + 63) // 64
+    ws = gpu_lib.new_workspace(w.B, w.H, w.N, w.d)
+    gpu_lib.sol_block_summaries(kd, vd, ws)
+    outs = []
+    for shift in (0, 1):
+        flat = torch.empty(w.B * w.H * nb * nb + 4, dtype=torch.float32, device=qd.device)
+        pm = flat[shift:shift + w.B * w.H * nb * nb].view(w.B, w.H, nb, nb)
+        assert (pm.data_ptr() % 16 == 0) == (shift == 0)
+        words = torch.zeros((w.B, w.H, nb, W), dtype=torch.int64, device=qd.device)
+        gpu_lib.sol_route(qd, gpu_lib.SOL_ROUTE_THRESHOLD, ws, pm, words, beta=1.0)
+        torch.cuda.synchronize()
+        outs.append((pm.clone(), words.clone()))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])

@@ -502,13 +502,13 @@ def main() -> int:
     torch.cuda.synchronize()
 
     def stepper(beta, flags):
-        pre = lambda: sb.sol_block_summaries(kd, vd, ws)
+        pre = lambda: sb.sol_block_summaries(kd, vd, ws, flags)
         fused = lambda: sb.sol_attn_fused(qd, kd, vd, out, beta, flags, ws)
         return pre, fused
 
     def measure(beta, flags, steps, warmup):
         # untimed call with stats: kept blocks (the algorithmic work) of this setting
-        sb.sol_block_summaries(kd, vd, ws)
+        sb.sol_block_summaries(kd, vd, ws, flags)
         sb.sol_attn_fused(qd, kd, vd, out, beta, flags, ws, kept_per_row=kept)
         torch.cuda.synchronize()
         n_kept = int(kept.sum().item())
@@ -540,6 +540,11 @@ def main() -> int:
     balance = load_balance(sb, qd, kd, vd, out, ws, args.beta, corr, w)
     ablation = routing_overhead(sb, qd, kd, vd, out, ws, args.beta, w, max(3, args.steps // 2))
     rowc = None if args.no_correction else measure(args.beta, sb.SOL_CORRECTION_ROW, max(3, args.steps // 2), 3)
+    # the low-memory mode (no V^T copy; value tiles from V with transposing LDS reads)
+    lowmem = measure(args.beta, corr | sb.SOL_LOW_MEMORY, max(3, args.steps // 2), 3)
+    lowmem["workspace_bytes"] = sb.sol_attn_workspace_bytes(w.B, w.H, w.N, w.d, sb.SOL_LOW_MEMORY)
+    lowmem["default_workspace_bytes"] = sb.sol_attn_workspace_bytes(w.B, w.H, w.N, w.d)
+    lowmem["bit_equal_to_default"] = bool(torch.equal(out, ref))   # same beta and correction
     study = None if args.no_routing_study else routing_study(sb, qd, kd, vd, out, ws, w, 5)
     if study is not None:
         # like for like: the in-pass routing's cost inside the fused pass (fused pass without
@@ -608,6 +613,7 @@ def main() -> int:
         "load_balance": balance,
         "routing_ablation": ablation,
         "row_correction": rowc,
+        "low_memory": lowmem,
         "routing_study": study,
         "prepass": prepass_report(w, head["prepass_ms"]),
         "configs": configs,

@@ -30,6 +30,7 @@ SOL_CORRECTION = 0x2
 SOL_DENSE = 0x4
 SOL_SYNC = 0x8
 SOL_CORRECTION_ROW = 0x10
+SOL_LOW_MEMORY = 0x20
 
 SOL_ROUTE_THRESHOLD = 0
 SOL_ROUTE_TOPK = 1
@@ -58,7 +59,7 @@ class sol_strides(ctypes.Structure):
 class sol_workspace_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("total_bytes", "kbar_t", "kbar", "vsum", "kmean", "kcov", "vt", "qbar", "kbar_bf",
-                  "vbar_t", "scratch")]
+                  "vbar_t", "scratch", "vbar_bf")]
 
 
 _lib = None
@@ -79,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sol_last_error.restype = ctypes.c_char_p
     lib.sol_attn_workspace_bytes.argtypes = [i, i, i, i]
     lib.sol_attn_workspace_bytes.restype = sz
+    lib.sol_attn_workspace_bytes_flags.argtypes = [i, i, i, i, ctypes.c_uint]
+    lib.sol_attn_workspace_bytes_flags.restype = sz
     lib.sol_attn_workspace_layout.argtypes = [i, i, i, i, ctypes.POINTER(sol_workspace_layout)]
     lib.sol_attn_workspace_layout.restype = i
     lib.sol_block_summaries.argtypes = [vp, vp, i, i, i, i, u, vp, sz, vp]
@@ -121,8 +124,9 @@ def sol_last_error() -> str:
     return load_library().sol_last_error().decode()
 
 
-def sol_attn_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
-    return load_library().sol_attn_workspace_bytes(B, H, N, d)
+def sol_attn_workspace_bytes(B: int, H: int, N: int, d: int, flags: int = 0) -> int:
+    """Workspace bytes for the shape and the calls' flags (SOL_LOW_MEMORY: no V^T copy)."""
+    return load_library().sol_attn_workspace_bytes_flags(B, H, N, d, flags)
 
 
 def sol_attn_workspace_layout(B: int, H: int, N: int, d: int) -> sol_workspace_layout:
@@ -205,9 +209,9 @@ def _dbg(kept_per_row=None, mask_bits=None, tau=None, item_clock=None):
     return ctypes.byref(sol_debug(ptr(kept_per_row), ptr(mask_bits), ptr(tau), ptr(item_clock)))
 
 
-def new_workspace(B: int, H: int, N: int, d: int, device=None) -> torch.Tensor:
-    """A uint8 device tensor of sol_attn_workspace_bytes bytes."""
-    n = sol_attn_workspace_bytes(B, H, N, d)
+def new_workspace(B: int, H: int, N: int, d: int, device=None, flags: int = 0) -> torch.Tensor:
+    """A uint8 device tensor of sol_attn_workspace_bytes bytes (for the calls' flags)."""
+    n = sol_attn_workspace_bytes(B, H, N, d, flags)
     if n == 0:
         raise ValueError("invalid or unsupported shape")
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
@@ -219,15 +223,17 @@ def workspace_views(ws: torch.Tensor, B: int, H: int, N: int, d: int) -> Dict[st
     nb = N // BLOCK
     nbp = (nb + 3) // 4 * 4
     f32 = lambda off, shape: ws[off:off + 4 * math.prod(shape)].view(torch.float32).view(shape)
-    return {
+    views = {
         "kbar_t": f32(lay.kbar_t, (B, H, d, nbp))[..., :nb],
         "kbar": f32(lay.kbar, (B, H, nb, d)),
         "vsum": f32(lay.vsum, (B, H, nb, d)),
         "kmean": f32(lay.kmean, (B, H, d)),
         "kcov": f32(lay.kcov, (B, H, d, d)),
-        "vt": ws[lay.vt:lay.vt + 2 * B * H * N * d].view(torch.bfloat16).view(B, H, nb, d, BLOCK),
         "qbar": f32(lay.qbar, (B, H, nb, d)),
     }
+    if ws.numel() >= lay.vt + 2 * B * H * N * d:   # not a low-memory workspace
+        views["vt"] = ws[lay.vt:lay.vt + 2 * B * H * N * d].view(torch.bfloat16).view(B, H, nb, d, BLOCK)
+    return views
 
 
 def sol_block_summaries(k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor,
@@ -315,7 +321,7 @@ def sol_attn_fwd_ex(q, k, v, out, beta: float, flags: int, stream=None,
     _dev(q, k, v, out)
     flags |= _dtype_flag(q, k, v, out)
     if workspace is None:
-        workspace = new_workspace(B, H, N, d, q.device)
+        workspace = new_workspace(B, H, N, d, q.device, flags)
     _dev(workspace)
     _check(load_library().sol_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                           B, H, N, d, float(beta), flags, _stream(stream),
@@ -356,7 +362,7 @@ def sol_attn_fwd_strided(q, k, v, out, beta: float, flags: int, stream=None,
     sq, sk, sv, so = _strides(q), _strides(k), _strides(v), _strides(out)
     flags |= _dtype_flag(q, k, v, out)
     if workspace is None:
-        workspace = new_workspace(B, H, N, d, q.device)
+        workspace = new_workspace(B, H, N, d, q.device, flags)
     _check(load_library().sol_attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                                B, H, N, d, sq, sk, sv, so, float(beta), flags,
                                                _stream(stream), workspace.data_ptr(), _ws_bytes(workspace),

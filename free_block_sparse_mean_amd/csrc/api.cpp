@@ -25,12 +25,13 @@ Layout make_layout(const Shape& s) {
   L.vsum = off;     off += up256(bh * nb * d * 4);
   L.kmean = off;    off += up256(bh * d * 4);
   L.kcov = off;     off += up256(bh * d * d * 4);
-  L.vt = off;       off += up256(bh * nb * d * 64 * 2);
   L.qbar = off;     off += up256(bh * nb * d * 4);
   L.kbar_bf = off;  off += up256(bh * (size_t)s.n_words * 64 * d * 2);
   L.vbar_t = off;   off += up256(bh * (size_t)s.n_words * 64 * d * 2);
+  L.vbar_bf = off;  off += up256(bh * (size_t)s.n_words * 64 * d * 2);
   L.s1_part = off;  off += up256(bh * (size_t)s.cov_parts * d * 8);
   L.s2_part = off;  off += up256(bh * (size_t)s.cov_parts * d * d * 8);
+  L.vt = off;       off += up256(bh * nb * d * 64 * 2);
   L.total = off;
   return L;
 }
@@ -48,6 +49,7 @@ Workspace bind_workspace(const Shape& s, void* base) {
   w.qbar = reinterpret_cast<float*>(b + L.qbar);
   w.kbar_bf = reinterpret_cast<__bf16*>(b + L.kbar_bf);
   w.vbar_t = reinterpret_cast<__bf16*>(b + L.vbar_t);
+  w.vbar_bf = reinterpret_cast<__bf16*>(b + L.vbar_bf);
   w.s1_part = reinterpret_cast<double*>(b + L.s1_part);
   w.s2_part = reinterpret_cast<double*>(b + L.s2_part);
   return w;
@@ -137,9 +139,16 @@ sol_status check_dbg_align(const sol_debug* dbg) {
   return check_align(dbg->item_clock, 8, "item_clock");
 }
 
-// A caller workspace: present, large enough for the shape, 256-byte aligned.
-sol_status check_workspace(const sol::Shape& s, const void* ws, size_t ws_bytes) {
-  const size_t need = sol::make_layout(s).total;
+// Workspace bytes of a shape: the whole layout, or with SOL_LOW_MEMORY the
+// part before the V^T copy (the last array).
+size_t ws_need(const sol::Shape& s, unsigned flags) {
+  const sol::Layout L = sol::make_layout(s);
+  return (flags & SOL_LOW_MEMORY) ? L.vt : L.total;
+}
+
+// A caller workspace: present, large enough for the shape and mode, 256-byte aligned.
+sol_status check_workspace(const sol::Shape& s, const void* ws, size_t ws_bytes, unsigned flags) {
+  const size_t need = ws_need(s, flags);
   if (!ws || ws_bytes < need)
     return fail(SOL_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, ws_bytes, ws ? "" : ", NULL");
   return check_align(ws, 256, "workspace");
@@ -159,7 +168,7 @@ sol_status summaries_checked(const sol::Shape& s, const void* k, const void* v, 
                              void* ws, hipStream_t st, const sol::IoStrides* io = nullptr) {
   const sol::Workspace w = sol::bind_workspace(s, ws);
   const sol::IoStrides x = io ? *io : sol::contiguous_io(s);
-  hipError_t e = sol::launch_prepass(s, dtype_of(flags), k, v, x.k, x.v, w, st);
+  hipError_t e = sol::launch_prepass(s, dtype_of(flags), k, v, x.k, x.v, w, !(flags & SOL_LOW_MEMORY), st);
   if (e != hipSuccess) return device_fail(e, "block-summary pre-pass launch");
   return SOL_OK;
 }
@@ -183,6 +192,7 @@ sol_status fused_checked(const sol::Shape& s, const void* q, const void* k, cons
   a.mask_in = nullptr;
   a.text_blocks = text_blocks;
   a.io = io ? *io : sol::contiguous_io(s);
+  a.low_memory = (flags & SOL_LOW_MEMORY) != 0;
   hipError_t e = sol::launch_fused(s, dtype_of(flags), a, st);
   if (e != hipSuccess) return device_fail(e, "fused kernel launch");
   return SOL_OK;
@@ -250,6 +260,15 @@ size_t sol_attn_workspace_bytes(int B, int H, int N, int d) {
   return st == SOL_OK ? sol::make_layout(s).total : 0;
 }
 
+size_t sol_attn_workspace_bytes_flags(int B, int H, int N, int d, unsigned flags) {
+  sol::Shape s;
+  char saved[sizeof(g_err)];
+  memcpy(saved, g_err, sizeof(g_err));
+  const sol_status st = check_shape(B, H, N, d, &s);
+  memcpy(g_err, saved, sizeof(g_err));
+  return st == SOL_OK ? ws_need(s, flags) : 0;
+}
+
 sol_status sol_attn_workspace_layout(int B, int H, int N, int d, sol_workspace_layout* layout) {
   if (!layout) return fail(SOL_ERR_INVALID_ARG, "layout must be non-null");
   sol::Shape s;
@@ -267,6 +286,7 @@ sol_status sol_attn_workspace_layout(int B, int H, int N, int d, sol_workspace_l
   layout->kbar_bf = L.kbar_bf;
   layout->vbar_t = L.vbar_t;
   layout->scratch = L.s1_part;
+  layout->vbar_bf = L.vbar_bf;
   return ok();
 }
 
@@ -278,7 +298,7 @@ sol_status sol_block_summaries(const void* k, const void* v, int B, int H, int N
   if (!k || !v) return fail(SOL_ERR_INVALID_ARG, "k and v must be non-null");
   if ((st = check_flags(flags)) != SOL_OK) return st;
   if ((st = check_io_align(nullptr, k, v, nullptr)) != SOL_OK) return st;
-  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes, flags)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   if ((st = summaries_checked(s, k, v, flags, workspace, str)) != SOL_OK) return st;
   return finish(flags, str);
@@ -292,7 +312,7 @@ sol_status sol_attn_fused(const void* q, const void* k, const void* v, void* out
   if (st != SOL_OK) return st;
   if ((st = check_fused_args(q, k, v, out, beta, flags)) != SOL_OK) return st;
   if ((st = check_dbg_align(dbg)) != SOL_OK) return st;
-  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes, flags)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str)) != SOL_OK) return st;
   return finish(flags, str);
@@ -313,7 +333,7 @@ sol_status sol_attn_masked(const void* q, const void* k, const void* v, void* ou
   if ((st = check_io_align(q, k, v, out)) != SOL_OK) return st;
   if ((st = check_align(mask_bits, 8, "mask_bits")) != SOL_OK) return st;
   if ((st = check_align(kept_per_row, 4, "kept_per_row")) != SOL_OK) return st;
-  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes, flags)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   sol::FusedArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out;
@@ -329,6 +349,7 @@ sol_status sol_attn_masked(const void* q, const void* k, const void* v, void* ou
   a.mask_in = mask_bits;
   a.text_blocks = 0;
   a.io = sol::contiguous_io(s);
+  a.low_memory = (flags & SOL_LOW_MEMORY) != 0;
   hipError_t e = sol::launch_fused(s, dtype_of(flags), a, str);
   if (e != hipSuccess) return device_fail(e, "given-mask kernel launch");
   return finish(flags, str);
@@ -356,7 +377,7 @@ sol_status sol_route(const void* q, int B, int H, int N, int d, unsigned flags, 
   if ((st = check_align(mask_bits, 8, "mask_bits")) != SOL_OK) return st;
   if ((st = check_align(kept_per_row, 4, "kept_per_row")) != SOL_OK) return st;
   if ((st = check_align(topk_idx, 4, "topk_idx")) != SOL_OK) return st;
-  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes, flags)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   sol::RouteArgs a;
   a.q = q;
@@ -387,7 +408,7 @@ sol_status sol_attn_fused_joint(const void* q, const void* k, const void* v, voi
   if (text_blocks < 0 || text_blocks > s.n_b)
     return fail(SOL_ERR_INVALID_ARG, "text_blocks must be in [0, n_b] (got %d, n_b %d)", text_blocks, s.n_b);
   if ((st = check_dbg_align(dbg)) != SOL_OK) return st;
-  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes, flags)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str, text_blocks)) != SOL_OK) return st;
   return finish(flags, str);
@@ -401,7 +422,7 @@ sol_status sol_attn_fwd_ex(const void* q, const void* k, const void* v, void* ou
   if (st != SOL_OK) return st;
   if ((st = check_fused_args(q, k, v, out, beta, flags)) != SOL_OK) return st;
   if ((st = check_dbg_align(dbg)) != SOL_OK) return st;
-  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes, flags)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   if ((st = summaries_checked(s, k, v, flags, workspace, str)) != SOL_OK) return st;
   if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str)) != SOL_OK) return st;
@@ -423,7 +444,7 @@ sol_status sol_attn_fwd_strided(const void* q, const void* k, const void* v, voi
   if ((st = take_strides(s, flags, v_strides, v, "v", false, &io.v)) != SOL_OK) return st;
   if ((st = take_strides(s, flags, out_strides, out, "out", true, &io.o)) != SOL_OK) return st;
   if ((st = check_dbg_align(dbg)) != SOL_OK) return st;
-  if ((st = check_workspace(s, workspace, ws_bytes)) != SOL_OK) return st;
+  if ((st = check_workspace(s, workspace, ws_bytes, flags)) != SOL_OK) return st;
   hipStream_t str = static_cast<hipStream_t>(hip_stream);
   if ((st = summaries_checked(s, k, v, flags, workspace, str, &io)) != SOL_OK) return st;
   if ((st = fused_checked(s, q, k, v, out, beta, flags, workspace, dbg, str, 0, &io)) != SOL_OK) return st;
@@ -438,7 +459,7 @@ sol_status sol_attn_fwd_noalloc(const void* q, const void* k, const void* v, voi
   if (st != SOL_OK) return st;
   if ((st = check_fused_args(q, k, v, out, beta, flags)) != SOL_OK) return st;
   if ((st = check_dbg_align(dbg)) != SOL_OK) return st;
-  const size_t need = sol::make_layout(s).total;
+  const size_t need = ws_need(s, flags);
   if (need > sol::kNoAllocScratchBytes)
     return fail(SOL_ERR_UNSUPPORTED, "the shape needs %zu bytes of scratch, above the %zu-byte maximum of "
                 "sol_attn_fwd_noalloc (use sol_attn_fwd_ex with a workspace)", need, sol::kNoAllocScratchBytes);
@@ -457,7 +478,7 @@ sol_status sol_attn_fwd(const void* q, const void* k, const void* v, void* out, 
   sol_status st = check_shape(B, H, N, d, &s);
   if (st != SOL_OK) return st;
   if ((st = check_fused_args(q, k, v, out, beta, flags)) != SOL_OK) return st;
-  const size_t need = sol::make_layout(s).total;
+  const size_t need = ws_need(s, flags);
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

@@ -73,6 +73,7 @@ struct FusedParams {
   const __bf16* vt;
   const __bf16* kbar_bf;   // block-summary tiles for the per-row correction (bf16)
   const __bf16* vbar_t;
+  const __bf16* vbar_bf;   // the same v_bar tiles row-major (per-row correction, low-memory mode)
   const float* kbar;       // block means (fp32 per-row correction)
   const float* kbar_t;
   const float* vsum;
@@ -252,39 +253,51 @@ struct DmaLane {
   int k_off;         // byte offset of this lane's K chunk in slab 0 of a tile of the input K
   long long k_slab;  // bytes between slabs of the input K (16 or 32 rows; uniform)
   int kc_off;        // the same offset in a contiguous [64][D] tile (block summaries)
-  int v_off;         // byte offset of this lane's V^T chunk in slab 0
+  int v_off;         // byte offset of this lane's V^T chunk in slab 0, or (low-memory
+                     // mode) of its chunk of a row-major tile of the input V
+  long long v_slab;  // bytes between slabs of that V source (uniform)
   int wave_lds;      // this wave's first LDS byte inside a slab (uniform)
 };
-// k_row: row stride of the input K in elements
-template <int D>
-__device__ __forceinline__ DmaLane dma_lane(int t, long long k_row) {
+// k_row, v_row: row strides of the input K and V in elements. VRM: V tiles
+// row-major from the input V (same lane pattern and swizzle as K) instead of
+// the pre-pass's V^T blocks.
+template <int D, bool VRM>
+__device__ __forceinline__ DmaLane dma_lane(int t, long long k_row, long long v_row) {
   DmaLane dl;
   constexpr int RPS = 4096 / (D * 2);   // rows per 4096-byte slab
   if constexpr (D == 128) {
     const int r = t >> 4, c = (t & 15) ^ (r & 15);          // rows of 16 chunks
     dl.k_off = (int)(r * k_row * 2) + c * 16;
     dl.kc_off = r * D * 2 + c * 16;
+    if constexpr (VRM) dl.v_off = (int)(r * v_row * 2) + c * 16;
   } else {
     const int r = t >> 3, c = (t & 7) ^ ((r >> 1) & 7);     // rows of 8 chunks
     dl.k_off = (int)(r * k_row * 2) + c * 16;
     dl.kc_off = r * D * 2 + c * 16;
+    if constexpr (VRM) dl.v_off = (int)(r * v_row * 2) + c * 16;
   }
   dl.k_slab = RPS * k_row * 2;
-  const int d = t >> 3, kc = (t & 7) ^ ((d >> 1) & 7);      // V^T rows of 8 chunks
-  dl.v_off = d * 128 + kc * 16;
+  if constexpr (VRM) {
+    dl.v_slab = RPS * v_row * 2;
+  } else {
+    const int d = t >> 3, kc = (t & 7) ^ ((d >> 1) & 7);    // V^T rows of 8 chunks
+    dl.v_off = d * 128 + kc * 16;
+    dl.v_slab = 4096;
+  }
   dl.wave_lds = __builtin_amdgcn_readfirstlane((t >> 6) * 1024);
   return dl;
 }
 
-// bf16: start loading the K tile and the transposed V tile of key block j
-// straight into LDS buffer `buf`. The K source is either the input K (row
-// stride from the caller) or a contiguous tile of block summaries: k_off is
-// this lane's byte offset in the first slab of 4096 / (2 D) rows and k_slab
-// the byte distance between slabs. Completion is awaited with s_waitcnt vmcnt
-// before the next barrier.
+// bf16: start loading the K tile and the V tile (transposed, or row-major in
+// the low-memory mode) of key block j straight into LDS buffer `buf`. Each
+// source is either the input tensor (row stride from the caller), a block of
+// the V^T copy or a contiguous tile of block summaries: *_off is this lane's
+// byte offset in the first slab of 4096 bytes of LDS and *_slab the byte
+// distance between the slabs in the source. Completion is awaited with
+// s_waitcnt vmcnt before the next barrier.
 template <int D>
 __device__ __forceinline__ void issue_tile(unsigned char* buf, const __bf16* Ksrc, int k_off, long long k_slab,
-                                           const __bf16* Vsrc, const DmaLane& dl) {
+                                           const __bf16* Vsrc, int v_off, long long v_slab, const DmaLane& dl) {
   constexpr int NI = D / 32;   // slabs per region
   // Buffer-form loads: a scalar descriptor per region (base = the tile, size =
   // the tile's extent), this lane's fixed 32-bit offset and a scalar slab
@@ -294,7 +307,7 @@ __device__ __forceinline__ void issue_tile(unsigned char* buf, const __bf16* Ksr
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Ksrc), (short)0, (int)(NI * k_slab), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Vsrc), (short)0, NI * 4096, kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Vsrc), (short)0, (int)(NI * v_slab), kRsrcWord3);
 #pragma unroll
   for (int i = 0; i < NI; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t*)(buf + i * 4096 + dl.wave_lds), 16, (unsigned)k_off,
@@ -302,7 +315,7 @@ __device__ __forceinline__ void issue_tile(unsigned char* buf, const __bf16* Ksr
 #pragma unroll
   for (int i = 0; i < NI; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t*)(buf + Geom<__bf16, D>::kKBytes + i * 4096 + dl.wave_lds),
-                                             16, (unsigned)dl.v_off, (unsigned)(i * 4096), 0, 0);
+                                             16, (unsigned)v_off, (unsigned)(i * v_slab), 0, 0);
 }
 
 // fp32: stage the K and V tiles of key block j in LDS (synchronously)
@@ -326,17 +339,43 @@ __device__ __forceinline__ void commit_f32(float* stK, float* stV, const float* 
 // swizzles depend on the row only through lane % 16 (every 16-row sub-tile
 // starts at a multiple of 16), so one offset per k-step serves all
 // sub-tiles, which differ by compile-time displacements.
-template <int D> struct LaneOfs {
+//
+// VRM (low-memory mode): V tiles are row-major in LDS, with the K tiles'
+// swizzle, and each P.V A operand is gathered by two transposing reads
+// (ds_read_b64_tr_b16): within each group of 16 lanes, result lane i, element
+// e is element i % 4 of the 8 bytes source lane 4e + i / 4 points at. For
+// d-tile dt (16 head dims) and keys 32ks + 16h + 4g + e (g = lane / 16, the key
+// order of P), source lane 16g + j points at row 32ks + 16h + 4g + j / 4, head
+// dims 16dt + 4(j % 4) .. +3; in a swizzled row that is the address of d-tile
+// 0 with byte bits 5-7 flipped by dt, and rows 16 apart keep the swizzle.
+template <int D, bool VRM = false> struct LaneOfs {
+  static constexpr int kNV = VRM ? D / 16 : 2;
   int k[D / 32];   // K operand, k-step ks: row lane%16 of sub-tile 0, chunk 4ks + lane/16
-  int v[2];        // V^T operand, k-step ks: row lane%16 of d-tile 0, chunk 4ks + lane/16
+  int v[kNV];      // V^T operand, k-step ks: row lane%16 of d-tile 0, chunk 4ks + lane/16;
+                   // VRM: d-tile dt, the transposing read of k-step 0, half 0
   __device__ __forceinline__ explicit LaneOfs(int lane) {
     const int l16 = lane & 15, grp = lane >> 4;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) k[ks] = 16 * k_pos<D>(l16, ks * 4 + grp);
+    if constexpr (VRM) {
+      const int r0 = 4 * grp + (l16 >> 2);   // row within the 16-key half
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) v[ks] = Geom<__bf16, D>::kKBytes + 16 * v_pos(l16, ks * 4 + grp);
+      for (int dt = 0; dt < kNV; ++dt)
+        v[dt] = Geom<__bf16, D>::kKBytes + 16 * k_pos<D>(r0, 2 * dt + ((lane >> 1) & 1)) + 8 * (lane & 1);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) v[ks] = Geom<__bf16, D>::kKBytes + 16 * v_pos(l16, ks * 4 + grp);
+    }
   }
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// transposing LDS read of four bf16 at byte offset `off` of `buf` (see LaneOfs)
+__device__ __forceinline__ s16x4 tr_read(const unsigned char* buf, int off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) unsigned char*)(const_cast<unsigned char*>(buf)) + off));
+}
 
 // One tile of 64 keys for one query block of this wave: S^T = K Q^T, online
 // softmax in base 2, O^T += V^T P^T.
@@ -347,28 +386,30 @@ template <int D> struct LaneOfs {
 // XO: operand offsets of k-steps ks > 0 formed in the tile from those of
 // k-step 0 (4 fewer registers held across the walk, 4 more VALU per tile):
 // used where the register budget is tightest (the per-row correction).
-template <int D, bool VIRT = false, bool XO = false>
-__device__ __forceinline__ void tile_bf16(ExactState<__bf16, D>& st, const unsigned char* buf, const LaneOfs<D>& lo,
-                                          uint64_t excl = 0) {
+template <int D, bool VIRT = false, bool XO = false, bool VRM = false>
+__device__ __forceinline__ void tile_bf16(ExactState<__bf16, D>& st, const unsigned char* buf,
+                                          const LaneOfs<D, VRM>& lo, uint64_t excl = 0) {
   using S = ExactState<__bf16, D>;
+  constexpr int NV = LaneOfs<D, VRM>::kNV;
   // The XOR swizzles make the chunk index of k-step ks that of k-step 0 with
-  // bits 2-3 flipped by ks, i.e. byte offset bits 6-7 (K) or bit 6 (V^T); the
-  // empty asm keeps the compiler from hoisting the derived offsets out of the
-  // walk.
-  int ko[S::KS], vo[2];
+  // bits 2-3 flipped by ks, i.e. byte offset bits 6-7 (K) or bit 6 (V^T), and
+  // (VRM) the V offset of d-tile dt that of d-tile 0 with bits 5-7 flipped by
+  // dt; the empty asm keeps the compiler from hoisting the derived offsets
+  // out of the walk.
+  int ko[S::KS], vo[NV];
   if constexpr (XO) {
     int k0 = lo.k[0], v0 = lo.v[0];
     asm volatile("" : "+v"(k0), "+v"(v0));
 #pragma unroll
     for (int ks = 0; ks < S::KS; ++ks) ko[ks] = k0 ^ (64 * ks);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      vo[ks] = Geom<__bf16, D>::kKBytes + ((v0 - Geom<__bf16, D>::kKBytes) ^ (64 * ks));
+    for (int i = 0; i < NV; ++i)
+      vo[i] = VRM ? (v0 ^ (32 * i)) : Geom<__bf16, D>::kKBytes + ((v0 - Geom<__bf16, D>::kKBytes) ^ (64 * i));
   } else {
 #pragma unroll
     for (int ks = 0; ks < S::KS; ++ks) ko[ks] = lo.k[ks];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) vo[ks] = lo.v[ks];
+    for (int i = 0; i < NV; ++i) vo[i] = lo.v[i];
   }
   constexpr float kScale2 = inv_sqrt(D) * kLog2e;   // logit -> base-2 exponent
   constexpr float kOff = VIRT ? 6.0f : 0.0f;        // log2 of the multiplicity
@@ -448,12 +489,22 @@ __device__ __forceinline__ void tile_bf16(ExactState<__bf16, D>& st, const unsig
   st.lrow = l;
   // O^T (d x 16 queries) += V^T (d x 64 keys) P^T in two k-steps of 32 keys;
   // V^T columns are stored in operand order; d-tiles are 16 rows of 8 chunks
-  // = 2048 bytes apart
+  // = 2048 bytes apart. VRM: each A operand is two transposing reads of the
+  // row-major V tile (keys 32ks + 4g + 0..3, then the same + 16; rows 16
+  // apart are 32 D bytes apart).
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
     for (int dt = 0; dt < S::NACC; ++dt) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(buf + vo[ks] + dt * 2048);
+      bf16x8 a;
+      if constexpr (VRM) {
+        constexpr int kRow = 2 * D;
+        const s16x4 lo4 = tr_read(buf, vo[dt] + 32 * ks * kRow);
+        const s16x4 hi4 = tr_read(buf, vo[dt] + (32 * ks + 16) * kRow);
+        a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {
+        a = *reinterpret_cast<const bf16x8*>(buf + vo[ks] + dt * 2048);
+      }
       st.oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[ks], st.oacc[dt], 0, 0, 0);
     }
   }
@@ -555,7 +606,9 @@ __device__ __forceinline__ void epilogue(ExactState<T, D>& st, const FusedParams
 // blocks enter as tiles of block summaries in the walk).
 constexpr int kModeRoute = 0, kModeCorr = 1, kModeGiven = 2, kModeCorrRow = 3;
 
-template <typename T, int D, int MODE>
+// LM (bf16 only): low-memory mode, value tiles from the input V (row-major,
+// transposing operand reads) instead of the pre-pass's V^T copy.
+template <typename T, int D, int MODE, bool LM = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel(FusedParams p) {
   constexpr bool CORR = MODE == kModeCorr;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -997,8 +1050,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // barrier (all lanes' loads landed; every wave finished the previous tile,
     // so the other buffer is free), start loading the next union tile into
     // it, compute tile j.
-    const LaneOfs<D> lofs(lane);
-    const DmaLane dl = dma_lane<D>(t, p.ks.n);
+    const LaneOfs<D, LM> lofs(lane);
+    const DmaLane dl = dma_lane<D, LM>(t, p.ks.n, p.vs.n);
     constexpr bool kXO = MODE == kModeCorrRow;   // register budget: see tile_bf16
     ExactState<T, D> sts[kGMax];
 #pragma unroll
@@ -1035,7 +1088,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       return wi * 64 + (int)__builtin_ctzll(word);
     };
-    const __bf16* Vt = p.vt + (size_t)bh * n_b * D * 64;
+    // value tile of key block j: a block of the V^T copy, or (LM) rows of V
+    auto vtile = [&](int jj) -> const __bf16* {
+      if constexpr (LM) return reinterpret_cast<const __bf16*>(Vh) + (long long)jj * kBlock * p.vs.n;
+      else return p.vt + ((size_t)bh * n_b + jj) * D * 64;
+    };
 // s_waitcnt vmcnt(0) through the builtin, so the compiler's own wait tracking
 // knows the tile loads have landed (gfx9 encoding: vmcnt in bits 3:0, expcnt
 // 6:4 and lgkmcnt 11:8 left at their maxima)
@@ -1055,13 +1112,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       __builtin_amdgcn_s_barrier();                                               \
       asm volatile("" ::: "memory");                                              \
       if (nj >= 0)                                                                \
-        issue_tile<D>(NEXTB, Kh + (long long)nj * kBlock * p.ks.n, dl.k_off, dl.k_slab, Vt + (size_t)nj * D * 64, dl); \
+        issue_tile<D>(NEXTB, Kh + (long long)nj * kBlock * p.ks.n, dl.k_off, dl.k_slab, vtile(nj), dl.v_off, dl.v_slab, dl); \
       _Pragma("unroll") for (int g = 0; g < kGMax; ++g)                           \
-        if (keep & (1u << g)) tile_bf16<D, false, kXO>(sts[g], CURB, lofs);      \
+        if (keep & (1u << g)) tile_bf16<D, false, kXO, LM>(sts[g], CURB, lofs);  \
       j = nj;                                                                     \
     }
     int j = union_next(-1);
-    if (j >= 0) issue_tile<D>(sbufA, Kh + (long long)j * kBlock * p.ks.n, dl.k_off, dl.k_slab, Vt + (size_t)j * D * 64, dl);
+    if (j >= 0) issue_tile<D>(sbufA, Kh + (long long)j * kBlock * p.ks.n, dl.k_off, dl.k_slab, vtile(j), dl.v_off, dl.v_slab, dl);
     while (j >= 0) {
       SOL_STEP(sbufA, sbufB)
       if (j < 0) break;
@@ -1072,12 +1129,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // v_bar_j of 64 key blocks each) go through the same online softmax,
       // every block of the group taking the key blocks it did not keep.
       const __bf16* Kbs = p.kbar_bf + (size_t)bh * n_words * 64 * D;
-      const __bf16* Vbs = p.vbar_t + (size_t)bh * n_words * D * 64;
+      // value tiles: V^T order, or (LM) row-major, loaded like the K tiles
+      const __bf16* Vbs = (LM ? p.vbar_bf : p.vbar_t) + (size_t)bh * n_words * D * 64;
+      const int vb_off = LM ? dl.kc_off : dl.v_off;
       SOL_WAIT_VM();   // both buffers free: every load landed, every wave past its last tile
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      issue_tile<D>(sbufA, Kbs, dl.kc_off, 4096, Vbs, dl);
+      issue_tile<D>(sbufA, Kbs, dl.kc_off, 4096, Vbs, vb_off, 4096, dl);
 #define SOL_VSTEP(CURB, NEXTB)                                                    \
       {                                                                           \
         const uint64_t pad = (c == n_words - 1 && (n_b & 63)) ? ~0ull << (n_b & 63) : 0ull; \
@@ -1086,12 +1145,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_s_barrier();                                             \
         asm volatile("" ::: "memory");                                            \
         if (c + 1 < n_words)                                                      \
-          issue_tile<D>(NEXTB, Kbs + (size_t)(c + 1) * 64 * D, dl.kc_off, 4096, Vbs + (size_t)(c + 1) * D * 64, dl); \
+          issue_tile<D>(NEXTB, Kbs + (size_t)(c + 1) * 64 * D, dl.kc_off, 4096, Vbs + (size_t)(c + 1) * D * 64, vb_off, 4096, dl); \
         _Pragma("unroll") for (int g = 0; g < kGMax; ++g) {                       \
           uint64_t ex = g < nG ? (masks[g * n_words + c] | pad) : ~0ull;          \
           ex = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ex >> 32)) << 32) | \
                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ex);   /* uniform */ \
-          if (ex != ~0ull) tile_bf16<D, true, kXO>(sts[g], CURB, lofs, ex);       \
+          if (ex != ~0ull) tile_bf16<D, true, kXO, LM>(sts[g], CURB, lofs, ex);   \
         }                                                                         \
         ++c;                                                                      \
       }
@@ -1175,7 +1234,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // This translation unit holds only the bf16 kernels of the per-row correction
 // (built with the max-ILP scheduler, under which their register demand fits
 // without spills; the other kernels run faster under the default one).
-const void* fused_row_kernel_bf16(int d) {
+const void* fused_row_kernel_bf16(int d, bool low_memory) {
+  if (low_memory)
+    return d == 64 ? (const void*)fused_kernel<__bf16, 64, kModeCorrRow, true>
+                   : (const void*)fused_kernel<__bf16, 128, kModeCorrRow, true>;
   return d == 64 ? (const void*)fused_kernel<__bf16, 64, kModeCorrRow>
                  : (const void*)fused_kernel<__bf16, 128, kModeCorrRow>;
 }
@@ -1189,14 +1251,21 @@ const void* fused_row_reset_kernel() { return (const void*)queue_reset_kernel; }
 // a slot.
 QueueSlots g_queue_slots;
 
-template <typename T, int D>
-const void* kernel_for(const FusedArgs& a) {
-  if (a.mask_in) return (const void*)fused_kernel<T, D, kModeGiven>;
+template <typename T, int D, bool LM>
+const void* kernel_for_lm(const FusedArgs& a) {
+  if (a.mask_in) return (const void*)fused_kernel<T, D, kModeGiven, LM>;
   if (a.correction_row) {
-    if constexpr (std::is_same<T, __bf16>::value) return fused_row_kernel_bf16(D);   // own translation unit
+    if constexpr (std::is_same<T, __bf16>::value) return fused_row_kernel_bf16(D, LM);   // own translation unit
     else return (const void*)fused_kernel<T, D, kModeCorrRow>;
   }
-  return a.correction ? (const void*)fused_kernel<T, D, kModeCorr> : (const void*)fused_kernel<T, D, kModeRoute>;
+  return a.correction ? (const void*)fused_kernel<T, D, kModeCorr, LM> : (const void*)fused_kernel<T, D, kModeRoute, LM>;
+}
+// the low-memory mode changes only the bf16 value tiles (fp32 stages V from the input)
+template <typename T, int D>
+const void* kernel_for(const FusedArgs& a) {
+  if constexpr (std::is_same<T, __bf16>::value)
+    if (a.low_memory) return kernel_for_lm<T, D, true>(a);
+  return kernel_for_lm<T, D, false>(a);
 }
 
 template <typename T, int D>
@@ -1208,6 +1277,7 @@ hipError_t fused_impl(const Shape& s, const FusedArgs& a, hipStream_t st) {
   p.vt = a.ws.vt;
   p.kbar_bf = a.ws.kbar_bf;
   p.vbar_t = a.ws.vbar_t;
+  p.vbar_bf = a.ws.vbar_bf;
   p.kbar = a.ws.kbar;
   p.kbar_t = a.ws.kbar_t; p.vsum = a.ws.vsum; p.kmean = a.ws.kmean; p.kcov = a.ws.kcov;
   p.n_b = s.n_b; p.n_b_pad = s.n_b_pad; p.n_words = s.n_words;

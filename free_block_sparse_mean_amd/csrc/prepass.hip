@@ -239,21 +239,26 @@ __global__ __launch_bounds__(256) void moments_reduce_kernel(const double* __res
 // Block summaries as bf16 MFMA tiles, for the per-row correction: chunk c of
 // 64 key blocks gives a K-like tile [64][D] of k_bar_j and a V^T-like tile
 // [D][64] of v_bar_j = vsum_j / 64 in the column order of the V^T tiles; rows
-// and columns past n_b are zero (the fused pass masks them out). blockIdx.z
-// takes a quarter of the head dims.
+// and columns past n_b are zero (the fused pass masks them out); and the same
+// v_bar_j as a row-major [64][D] tile (write_rm: the low-memory mode's value tiles).
+// blockIdx.z takes a quarter of the head dims.
 template <int D>
 __global__ __launch_bounds__(256) void virtual_tiles_kernel(const float* __restrict__ kbar,
                                                             const float* __restrict__ vsum,
                                                             __bf16* __restrict__ kbar_bf,
-                                                            __bf16* __restrict__ vbar_t, int n_b,
-                                                            int n_chunks) {
+                                                            __bf16* __restrict__ vbar_t,
+                                                            __bf16* __restrict__ vbar_bf, int n_b,
+                                                            int n_chunks, int write_rm) {
   constexpr int DQ = D / 4;   // head dims of this workgroup
   const int c = blockIdx.x, t = threadIdx.x, d0 = blockIdx.z * DQ;
   const long long bh = blockIdx.y;
   __bf16* kd = kbar_bf + ((size_t)bh * n_chunks + c) * 64 * D;
+  __bf16* vr = vbar_bf + ((size_t)bh * n_chunks + c) * 64 * D;
   for (int e = t; e < 64 * DQ; e += 256) {
     const int r = e / DQ, dd = d0 + e % DQ, j = 64 * c + r;
     kd[r * D + dd] = j < n_b ? to_bf16(kbar[((size_t)bh * n_b + j) * D + dd]) : to_bf16(0.f);
+    if (write_rm)
+      vr[r * D + dd] = j < n_b ? to_bf16(vsum[((size_t)bh * n_b + j) * D + dd] * (1.0f / kBlock)) : to_bf16(0.f);
   }
   __bf16* vd = vbar_t + ((size_t)bh * n_chunks + c) * D * 64;
   for (int e = d0 * 64 + t; e < (d0 + DQ) * 64; e += 256) {
@@ -265,12 +270,17 @@ __global__ __launch_bounds__(256) void virtual_tiles_kernel(const float* __restr
 
 template <typename T, int D>
 hipError_t prepass_impl(const Shape& s, const void* k, const void* v, const TStrides& ks, const TStrides& vs,
-                        const Workspace& ws, hipStream_t st) {
+                        const Workspace& ws, bool write_vt, hipStream_t st) {
   const unsigned bh = (unsigned)s.BH();
   constexpr bool kVT = std::is_same<T, __bf16>::value;
-  hipLaunchKernelGGL((block_sums_kernel<T, D, kVT>), dim3((s.n_b + 3) / 4, bh), dim3(256), 0, st,
-                     static_cast<const T*>(k), static_cast<const T*>(v), ws.kbar, ws.vsum, ws.vt,
-                     s.n_b, s.H, ks, vs);
+  if (kVT && write_vt)
+    hipLaunchKernelGGL((block_sums_kernel<T, D, kVT>), dim3((s.n_b + 3) / 4, bh), dim3(256), 0, st,
+                       static_cast<const T*>(k), static_cast<const T*>(v), ws.kbar, ws.vsum, ws.vt,
+                       s.n_b, s.H, ks, vs);
+  else
+    hipLaunchKernelGGL((block_sums_kernel<T, D, false>), dim3((s.n_b + 3) / 4, bh), dim3(256), 0, st,
+                       static_cast<const T*>(k), static_cast<const T*>(v), ws.kbar, ws.vsum, ws.vt,
+                       s.n_b, s.H, ks, vs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((moments_partial_kernel<D>), dim3(s.cov_parts, bh, 2), dim3(256), 0, st, ws.kbar,
@@ -278,7 +288,7 @@ hipError_t prepass_impl(const Shape& s, const void* k, const void* v, const TStr
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if constexpr (kVT) {
     hipLaunchKernelGGL((virtual_tiles_kernel<D>), dim3(s.n_words, bh, 4), dim3(256), 0, st, ws.kbar, ws.vsum,
-                       ws.kbar_bf, ws.vbar_t, s.n_b, s.n_words);
+                       ws.kbar_bf, ws.vbar_t, ws.vbar_bf, s.n_b, s.n_words, write_vt ? 0 : 1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL((moments_reduce_kernel<D>), dim3((D * D + 255) / 256, bh), dim3(256), 0, st,
@@ -289,12 +299,12 @@ hipError_t prepass_impl(const Shape& s, const void* k, const void* v, const TStr
 }  // namespace
 
 hipError_t launch_prepass(const Shape& s, Dtype dt, const void* k, const void* v, const TStrides& ks,
-                          const TStrides& vs, const Workspace& ws, hipStream_t stream) {
+                          const TStrides& vs, const Workspace& ws, bool write_vt, hipStream_t stream) {
   if (dt == Dtype::BF16)
-    return s.d == 64 ? prepass_impl<__bf16, 64>(s, k, v, ks, vs, ws, stream)
-                     : prepass_impl<__bf16, 128>(s, k, v, ks, vs, ws, stream);
-  return s.d == 64 ? prepass_impl<float, 64>(s, k, v, ks, vs, ws, stream)
-                   : prepass_impl<float, 128>(s, k, v, ks, vs, ws, stream);
+    return s.d == 64 ? prepass_impl<__bf16, 64>(s, k, v, ks, vs, ws, write_vt, stream)
+                     : prepass_impl<__bf16, 128>(s, k, v, ks, vs, ws, write_vt, stream);
+  return s.d == 64 ? prepass_impl<float, 64>(s, k, v, ks, vs, ws, write_vt, stream)
+                   : prepass_impl<float, 128>(s, k, v, ks, vs, ws, write_vt, stream);
 }
 
 }  // namespace sol

@@ -54,12 +54,15 @@ struct Workspace {
   float* qbar;      // [BH][n_b][d]      block-mean queries (routing baselines only)
   __bf16* kbar_bf;  // [BH][n_words][64][d]  k_bar as bf16 tiles (per-row correction; bf16 only)
   __bf16* vbar_t;   // [BH][n_words][d][64]  v_bar as bf16 V^T-order tiles (per-row correction)
+  __bf16* vbar_bf;  // [BH][n_words][64][d]  v_bar as bf16 row-major tiles (per-row correction, low memory)
   double* s1_part;  // [BH][cov_parts][d]     (pre-pass scratch)
   double* s2_part;  // [BH][cov_parts][d][d]  (pre-pass scratch)
 };
 
 struct Layout {
-  size_t kbar_t, kbar, vsum, kmean, kcov, vt, qbar, kbar_bf, vbar_t, s1_part, s2_part, total;
+  // vt is the last array: the workspace of the low-memory mode (no V^T copy)
+  // is the first `vt` bytes of the full one
+  size_t kbar_t, kbar, vsum, kmean, kcov, qbar, kbar_bf, vbar_t, vbar_bf, s1_part, s2_part, vt, total;
 };
 
 Layout make_layout(const Shape& s);
@@ -95,6 +98,7 @@ struct FusedArgs {
   const uint64_t* mask_in;   // non-null: caller-given selection, no routing and no correction
   int text_blocks;           // joint attention: the last text_blocks blocks are text (always exact)
   IoStrides io;              // element strides of q, k, v and out
+  bool low_memory;           // bf16: V tiles from the input V (transposing LDS reads), no V^T copy
 };
 
 // Routing baselines with a materialized proxy map (route.hip).
@@ -115,12 +119,13 @@ struct RouteArgs {
 };
 
 // Each returns the first HIP error of its launches (hipSuccess otherwise).
+// write_vt: write the bf16 V^T copy (not in the low-memory mode)
 hipError_t launch_prepass(const Shape& s, Dtype dt, const void* k, const void* v, const TStrides& ks,
-                          const TStrides& vs, const Workspace& ws, hipStream_t stream);
+                          const TStrides& vs, const Workspace& ws, bool write_vt, hipStream_t stream);
 hipError_t launch_fused(const Shape& s, Dtype dt, const FusedArgs& a, hipStream_t stream);
 // The bf16 per-row-correction fused kernel for head dim d (64 or 128), compiled
 // in a translation unit of its own (fused.hip with SOL_FUSED_ROW_TU).
-const void* fused_row_kernel_bf16(int d);
+const void* fused_row_kernel_bf16(int d, bool low_memory);
 // That translation unit's queue-slot reset kernel (its own slot pool).
 const void* fused_row_reset_kernel();
 hipError_t launch_route(const Shape& s, Dtype dt, const RouteArgs& a, hipStream_t stream);

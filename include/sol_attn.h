@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define SOL_ATTN_ABI_VERSION 3
+#define SOL_ATTN_ABI_VERSION 4
 
 typedef enum sol_status {
   SOL_OK = 0,
@@ -83,7 +83,14 @@ typedef enum sol_status {
 #define SOL_CORRECTION_ROW 0x10u /* correction with the per-row logit q_r . k_bar_j / sqrt(d)
                                     of every virtual token, instead of the block proxy
                                     s_hat_ij (implies SOL_CORRECTION)                         */
-#define SOL_FLAGS_ALL  0x1Fu
+#define SOL_LOW_MEMORY 0x20u /* bf16: no V^T copy in the workspace; the fused pass reads
+                                the value tiles from V itself (transposing LDS reads).
+                                A smaller workspace (sol_attn_workspace_bytes_flags); the
+                                same results bit for bit, some time more. Pass it to the
+                                pre-pass and to the fused pass alike: a workspace whose
+                                pre-pass ran with it holds no V^T for a pass without it.
+                                No effect for float32 inputs.                              */
+#define SOL_FLAGS_ALL  0x3Fu
 
 /* Optional per-call outputs, all device pointers owned by the caller, each may be NULL.
  * n_b = N / 64, W = ceil(n_b / 64).
@@ -110,17 +117,21 @@ typedef struct sol_debug {
  *   vsum    [BH][n_b][d]  block sums of values (= 64 * v_bar_j)
  *   kmean   [BH][d]       m = mean over j of k_bar_j
  *   kcov    [BH][d][d]    C = (1/n_b) sum_j (k_bar_j - m)(k_bar_j - m)^T
- *   vt      [BH][n_b][d][64] bfloat16: each 64 x d block of V transposed,
- *                         column c holding key 32*(c/32) + 4*g + s for
- *                         s = c%8 < 4, else 32*(c/32) + 16 + 4*g + s - 4,
- *                         with g = (c%32)/8 (written for bf16 inputs only)
  *   qbar    [BH][n_b][d]  block-mean queries, written by sol_route only
  *   kbar_bf [BH][W][64][d] bfloat16: k_bar_j of key blocks 64c .. 64c+63 as
  *                         tile c (zero past n_b), for SOL_CORRECTION_ROW
  *   vbar_t  [BH][W][d][64] bfloat16: v_bar_j of the same blocks, transposed,
  *                         columns in the vt key order (zero past n_b)
- *                         (both written by the pre-pass for bf16 inputs)
- * the remaining bytes are scratch of the pre-pass. */
+ *   vbar_bf [BH][W][64][d] bfloat16: v_bar_j of the same blocks, row-major
+ *                         (zero past n_b) (these three written by the pre-pass
+ *                         for bf16 inputs, vbar_bf with SOL_LOW_MEMORY only)
+ *   scratch .. vt         scratch of the pre-pass
+ *   vt      [BH][n_b][d][64] bfloat16, the last array: each 64 x d block of V
+ *                         transposed, column c holding key 32*(c/32) + 4*g + s
+ *                         for s = c%8 < 4, else 32*(c/32) + 16 + 4*g + s - 4,
+ *                         with g = (c%32)/8 (written for bf16 inputs unless
+ *                         SOL_LOW_MEMORY; a SOL_LOW_MEMORY workspace ends here,
+ *                         its size is the vt offset) */
 typedef struct sol_workspace_layout {
   size_t total_bytes;
   size_t kbar_t;
@@ -133,6 +144,7 @@ typedef struct sol_workspace_layout {
   size_t kbar_bf;
   size_t vbar_t;
   size_t scratch;
+  size_t vbar_bf;
 } sol_workspace_layout;
 
 /* ABI version of the loaded library (SOL_ATTN_ABI_VERSION it was built with). */
@@ -145,6 +157,10 @@ const char* sol_last_error(void);
 /* Workspace size in bytes for a problem, 0 if the shape is invalid or unsupported. */
 size_t sol_attn_workspace_bytes(int B, int H, int N, int d);
 
+/* The same for the calls' flags: with SOL_LOW_MEMORY, the bytes before the V^T
+ * copy (vt offset); otherwise sol_attn_workspace_bytes. */
+size_t sol_attn_workspace_bytes_flags(int B, int H, int N, int d, unsigned flags);
+
 /* Offsets of the pre-pass arrays inside the workspace (see sol_workspace_layout). */
 sol_status sol_attn_workspace_layout(int B, int H, int N, int d, sol_workspace_layout* layout);
 
@@ -152,8 +168,9 @@ sol_status sol_attn_workspace_layout(int B, int H, int N, int d, sol_workspace_l
  * into `workspace` (layout above). Source of m and C: page "Sol-Attn:
  * l'attenzione sparsa che sceglie al volo" (paithon.it), section "Una soglia
  * per ogni riga", last paragraph (mean of the compressed keys and their d x d
- * second-moment matrix). flags: SOL_F32 selects the dtype; other bits ignored.
- * workspace: device memory of at least sol_attn_workspace_bytes bytes. */
+ * second-moment matrix). flags: SOL_F32 selects the dtype, SOL_LOW_MEMORY
+ * leaves out the V^T copy; other bits ignored. workspace: device memory of at
+ * least sol_attn_workspace_bytes_flags(B, H, N, d, flags) bytes. */
 sol_status sol_block_summaries(const void* k, const void* v, int B, int H, int N, int d,
                                unsigned flags, void* workspace, size_t ws_bytes,
                                void* hip_stream);
@@ -296,7 +313,7 @@ sol_status sol_attn_fwd(const void* q, const void* k, const void* v, void* out,
  * pre-pass arrays go to a scratch array of 64 MiB in the library's static
  * device memory (one per GPU, held from library load until the process
  * ends), and the call allocates and frees nothing. Shapes whose workspace
- * (sol_attn_workspace_bytes) exceeds 64 MiB give SOL_ERR_UNSUPPORTED before
+ * (sol_attn_workspace_bytes_flags) exceeds 64 MiB give SOL_ERR_UNSUPPORTED before
  * any device work. Every call on one GPU uses that GPU's one scratch array,
  * whose contents the previous call leaves behind (nothing in it has to start
  * at zero): calls that may overlap on one GPU (on different streams, or a

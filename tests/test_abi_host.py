@@ -85,11 +85,30 @@ def test_layout_offsets(lib):
     from free_block_sparse_mean_amd import binding
     lay = binding.sol_workspace_layout()
     assert lib.sol_attn_workspace_layout(2, 3, 64 * 100, 128, ctypes.byref(lay)) == 0
-    offs = [lay.kbar_t, lay.kbar, lay.vsum, lay.kmean, lay.kcov, lay.vt, lay.qbar, lay.kbar_bf,
-            lay.vbar_t, lay.scratch]
-    assert offs == sorted(offs) and offs[0] == 0 and lay.total_bytes > lay.scratch
+    offs = [lay.kbar_t, lay.kbar, lay.vsum, lay.kmean, lay.kcov, lay.qbar, lay.kbar_bf,
+            lay.vbar_t, lay.vbar_bf, lay.scratch, lay.vt]
+    assert offs == sorted(offs) and offs[0] == 0 and lay.total_bytes > lay.vt
     assert all(o % 256 == 0 for o in offs)
     assert lay.kbar - lay.kbar_t >= 6 * 128 * 100 * 4
+    # the V^T copy is the last array: the low-memory workspace is everything before it
+    assert lay.total_bytes - lay.vt >= 6 * 100 * 128 * 64 * 2
+    assert lib.sol_attn_workspace_bytes(2, 3, 64 * 100, 128) == lay.total_bytes
+    assert lib.sol_attn_workspace_bytes_flags(2, 3, 64 * 100, 128, 0x20) == lay.vt
+    assert lib.sol_attn_workspace_bytes_flags(2, 3, 64 * 100, 128, 0x2) == lay.total_bytes
+
+
+def test_low_memory_workspace_validation(lib):
+    """A SOL_LOW_MEMORY call accepts a workspace of the smaller size; the same call
+    without the flag refuses it before any device call."""
+    p = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    small = lib.sol_attn_workspace_bytes_flags(1, 2, 4096, 128, 0x20)
+    full = lib.sol_attn_workspace_bytes(1, 2, 4096, 128)
+    assert 0 < small < full
+    assert lib.sol_block_summaries(p, p, 1, 2, 4096, 128, 0, p, small, None) == 5
+    assert "workspace" in lib.sol_last_error().decode()
+    assert lib.sol_attn_fused(p, p, p, p, 1, 2, 4096, 128, ctypes.c_float(1.0), 0x2, p, small, None, None) == 5
+    assert lib.sol_attn_fused(p, p, p, p, 1, 2, 4096, 128, ctypes.c_float(1.0), 0x40, p, small, None, None) == 1
+    assert "flag" in lib.sol_last_error().decode()
 
 
 def test_masked_validation(lib):

@@ -139,60 +139,73 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const T* __restrict__ k
 
 // Partial first and second moments of the key summaries over one chunk of
 // `chunk` blocks (a multiple of 32), in double; also writes the transposed
-// summaries kbar_t.
-// blockIdx.z picks half of the D x D partial (rows z*D/2 ..); thread (ty, tx)
-// holds rows z*D/2 + ty + 16r and columns tx + 16s, so the 16 threads of a
-// row group read 16 consecutive doubles of a staged summary (no bank
-// conflicts). The staged tile is converted to double once.
+// summaries kbar_t. One workgroup per (chunk, half z of the D x D partial):
+// rows z*D/2 .. z*D/2 + D/2 - 1 and every column, as 16 x 16 tiles that the
+// four waves share out (D = 128: wave w takes row tile w and all eight column
+// tiles). The partial is X^T X over the chunk's rows X_j = k_bar_j; it runs
+// on the fp64 MFMA (16x16x4: four key blocks per step), whose products of
+// float-valued doubles are exact, with operands read from the staged tile
+// (converted to double once).
 template <int D>
-__global__ __launch_bounds__(256) void moments_partial_kernel(const float* __restrict__ kbar,
-                                                              float* __restrict__ kbar_t,
-                                                              double* __restrict__ s1_part,
-                                                              double* __restrict__ s2_part,
-                                                              int n_b, int n_b_pad, int parts, int chunk) {
-  constexpr int TJ = 32;            // key blocks staged per step
-  constexpr int RR = D / 32;        // rows per thread (half of the D rows over 16 row groups)
-  constexpr int RC = D / 16;        // columns per thread
-  constexpr int kPitch = D + 1;     // doubles per staged row: the transposing reads hit distinct banks
-  __shared__ double tile[TJ * kPitch];
-  const int t = threadIdx.x, ty = t / 16, tx = t % 16;
-  const long long bh = blockIdx.y;
-  const int part = blockIdx.x, z = blockIdx.z;
+__device__ __forceinline__ void moments_partial_body(const float* __restrict__ kbar,
+                                                     float* __restrict__ kbar_t,
+                                                     double* __restrict__ s1_part,
+                                                     double* __restrict__ s2_part, int n_b, int n_b_pad,
+                                                     int parts, int chunk, long long bh, int part, int z,
+                                                     double* tile) {
+  constexpr int TJ = 32;               // key blocks staged per step
+  constexpr int kPitch = D + 1;        // doubles per staged row: the transposing reads hit distinct banks
+  constexpr int CT = D / 16;           // column tiles
+  constexpr int NT = (D / 32) * CT / 4;   // tiles per wave (half the row tiles x all column tiles, 4 waves)
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int i16 = lane & 15, kq = lane >> 4;   // MFMA operand lane: row/column i16 of key block kq
   const int j0 = part * chunk;
   const int j1 = min(n_b, j0 + chunk);
   const int r0 = z * (D / 2);
-  double acc[RR][RC];
+  f64x4 acc[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) acc[u] = f64x4{0.0, 0.0, 0.0, 0.0};
   double s1 = 0.0;
-#pragma unroll
-  for (int r = 0; r < RR; ++r)
-#pragma unroll
-    for (int c = 0; c < RC; ++c) acc[r][c] = 0.0;
 
+  // the next step's summaries are loaded into registers while the current
+  // step is computed
+  constexpr int NL = TJ * D / 256;   // staged values per thread
+  float nxt[NL];
+  auto fetch = [&](int jb) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = t + 256 * i, jj = e / D, c = e % D, j = jb + jj;
+      nxt[i] = j < j1 ? kbar[((size_t)bh * n_b + j) * D + c] : 0.f;
+    }
+  };
+  fetch(j0);
   for (int jb = j0; jb < j1; jb += TJ) {
-    __syncthreads();
-    for (int e = t; e < TJ * D; e += 256) {
-      const int jj = e / D, c = e % D, j = jb + jj;
-      tile[jj * kPitch + c] = j < j1 ? (double)kbar[((size_t)bh * n_b + j) * D + c] : 0.0;
+    __syncthreads();   // every read of the previous step's tile is done
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = t + 256 * i;
+      tile[(e / D) * kPitch + e % D] = (double)nxt[i];
     }
     __syncthreads();
+    if (jb + TJ < j1) fetch(jb + TJ);
     // this half's columns of kbar_t (exact: the doubles came from floats)
     for (int e = t; e < TJ * (D / 2); e += 256) {
       const int c = r0 + e / TJ, jj = e % TJ, j = jb + jj;
       if (j < j1) kbar_t[((size_t)bh * D + c) * n_b_pad + j] = (float)tile[jj * kPitch + c];
     }
-    const int nj = min(TJ, j1 - jb);
-    for (int jj = 0; jj < nj; ++jj) {
-      const double* row = tile + jj * kPitch;
-      double a[RR], b[RC];
+    if (z == 0 && t < D) {
+      const int nj = min(TJ, j1 - jb);
+      for (int jj = 0; jj < nj; ++jj) s1 += tile[jj * kPitch + t];
+    }
+    // rows past j1 were staged as zeros, so every step takes all TJ rows
+#pragma unroll 2
+    for (int jj = 0; jj < TJ; jj += 4) {
+      const double* row = tile + (jj + kq) * kPitch;
 #pragma unroll
-      for (int r = 0; r < RR; ++r) a[r] = row[r0 + ty + 16 * r];
-#pragma unroll
-      for (int c = 0; c < RC; ++c) b[c] = row[tx + 16 * c];
-#pragma unroll
-      for (int r = 0; r < RR; ++r)
-#pragma unroll
-        for (int c = 0; c < RC; ++c) acc[r][c] += a[r] * b[c];
-      if (z == 0 && t < D) s1 += row[t];
+      for (int u = 0; u < NT; ++u) {
+        const int g = w * NT + u, rt = g / CT, ct = g % CT;
+        acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(row[r0 + 16 * rt + i16], row[16 * ct + i16], acc[u], 0, 0, 0);
+      }
     }
   }
   // zero this half's row padding of kbar_t once per head
@@ -203,11 +216,16 @@ __global__ __launch_bounds__(256) void moments_partial_kernel(const float* __res
       kbar_t[((size_t)bh * D + c) * n_b_pad + j] = 0.f;
     }
   }
+  // the fp64 MFMA leaves row kq + 4 v of its tile, column i16, in item v of
+  // a lane (unlike the fp32 16x16 forms, whose items are consecutive rows)
   double* outp = s2_part + ((size_t)bh * parts + part) * D * D;
 #pragma unroll
-  for (int r = 0; r < RR; ++r)
+  for (int u = 0; u < NT; ++u) {
+    const int g = w * NT + u, rt = g / CT, ct = g % CT;
 #pragma unroll
-    for (int c = 0; c < RC; ++c) outp[(size_t)(r0 + ty + 16 * r) * D + tx + 16 * c] = acc[r][c];
+    for (int v = 0; v < 4; ++v)
+      outp[(size_t)(r0 + 16 * rt + kq + 4 * v) * D + 16 * ct + i16] = acc[u][v];
+  }
   if (z == 0 && t < D) s1_part[((size_t)bh * parts + part) * D + t] = s1;
 }
 
@@ -241,17 +259,17 @@ __global__ __launch_bounds__(256) void moments_reduce_kernel(const double* __res
 // [D][64] of v_bar_j = vsum_j / 64 in the column order of the V^T tiles; rows
 // and columns past n_b are zero (the fused pass masks them out); and the same
 // v_bar_j as a row-major [64][D] tile (write_rm: the low-memory mode's value tiles).
-// blockIdx.z takes a quarter of the head dims.
+// One workgroup per (chunk c, quarter q of the head dims).
 template <int D>
-__global__ __launch_bounds__(256) void virtual_tiles_kernel(const float* __restrict__ kbar,
-                                                            const float* __restrict__ vsum,
-                                                            __bf16* __restrict__ kbar_bf,
-                                                            __bf16* __restrict__ vbar_t,
-                                                            __bf16* __restrict__ vbar_bf, int n_b,
-                                                            int n_chunks, int write_rm) {
+__device__ __forceinline__ void virtual_tiles_body(const float* __restrict__ kbar,
+                                                   const float* __restrict__ vsum,
+                                                   __bf16* __restrict__ kbar_bf,
+                                                   __bf16* __restrict__ vbar_t,
+                                                   __bf16* __restrict__ vbar_bf, int n_b,
+                                                   int n_chunks, int write_rm, long long bh, int c,
+                                                   int q) {
   constexpr int DQ = D / 4;   // head dims of this workgroup
-  const int c = blockIdx.x, t = threadIdx.x, d0 = blockIdx.z * DQ;
-  const long long bh = blockIdx.y;
+  const int t = threadIdx.x, d0 = q * DQ;
   __bf16* kd = kbar_bf + ((size_t)bh * n_chunks + c) * 64 * D;
   __bf16* vr = vbar_bf + ((size_t)bh * n_chunks + c) * 64 * D;
   for (int e = t; e < 64 * DQ; e += 256) {
@@ -266,6 +284,31 @@ __global__ __launch_bounds__(256) void virtual_tiles_kernel(const float* __restr
     const int j = 64 * c + 32 * (kc >> 2) + 4 * (kc & 3) + 16 * (ee >> 2) + (ee & 3);
     vd[e] = j < n_b ? to_bf16(vsum[((size_t)bh * n_b + j) * D + dd] * (1.0f / kBlock)) : to_bf16(0.f);
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void moments_partial_kernel(const float* __restrict__ kbar,
+                                                              float* __restrict__ kbar_t,
+                                                              double* __restrict__ s1_part,
+                                                              double* __restrict__ s2_part, int n_b,
+                                                              int n_b_pad, int parts, int chunk) {
+  __shared__ double tile[32 * (D + 1)];
+  moments_partial_body<D>(kbar, kbar_t, s1_part, s2_part, n_b, n_b_pad, parts, chunk, blockIdx.y, blockIdx.x,
+                          blockIdx.z, tile);
+}
+
+// A launch of its own, without the moment kernel's LDS tile: these workgroups
+// are latency bound and need occupancy (sharing the moment kernel's launch,
+// and so its LDS footprint, made the pair slower than two launches).
+template <int D>
+__global__ __launch_bounds__(256) void virtual_tiles_kernel(const float* __restrict__ kbar,
+                                                            const float* __restrict__ vsum,
+                                                            __bf16* __restrict__ kbar_bf,
+                                                            __bf16* __restrict__ vbar_t,
+                                                            __bf16* __restrict__ vbar_bf, int n_b,
+                                                            int n_words, int write_rm) {
+  virtual_tiles_body<D>(kbar, vsum, kbar_bf, vbar_t, vbar_bf, n_b, n_words, write_rm, blockIdx.y, blockIdx.x,
+                        blockIdx.z);
 }
 
 template <typename T, int D>
@@ -286,7 +329,7 @@ hipError_t prepass_impl(const Shape& s, const void* k, const void* v, const TStr
   hipLaunchKernelGGL((moments_partial_kernel<D>), dim3(s.cov_parts, bh, 2), dim3(256), 0, st, ws.kbar,
                      ws.kbar_t, ws.s1_part, ws.s2_part, s.n_b, s.n_b_pad, s.cov_parts, s.cov_chunk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if constexpr (kVT) {
+  if constexpr (kVT) {   // fp32 inputs have no summary tiles
     hipLaunchKernelGGL((virtual_tiles_kernel<D>), dim3(s.n_words, bh, 4), dim3(256), 0, st, ws.kbar, ws.vsum,
                        ws.kbar_bf, ws.vbar_t, ws.vbar_bf, s.n_b, s.n_words, write_vt ? 0 : 1);
     if ((e = hipGetLastError()) != hipSuccess) return e;

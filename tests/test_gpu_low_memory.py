@@ -120,3 +120,16 @@ def test_low_memory_noalloc_larger_shape(gpu_lib):
     gpu_lib.sol_attn_fwd_noalloc(q, k, v, out, 1.5, flags)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("form", ["none", "block", "row"])
+def test_low_memory_f32_inputs(form, gpu_lib):
+    """float32 inputs have no V^T copy in either mode: the flag only shrinks the
+    workspace, and the results are bit for bit those of the default mode."""
+    w = wl.small("lm_f32_d128", 1, 2, 64 * 70, 128, dtype="f32", grid=(2, 35, 64))
+    q, k, v = (t.cuda() for t in wl.make_qkv(w))
+    base = gpu_lib.SOL_F32 | {"none": 0, "block": gpu_lib.SOL_CORRECTION, "row": gpu_lib.SOL_CORRECTION_ROW}[form]
+    ref = _run(gpu_lib, q, k, v, 1.0, base)
+    low = _run(gpu_lib, q, k, v, 1.0, base | gpu_lib.SOL_LOW_MEMORY)
+    for a, b, name in zip(ref, low, ("out", "kept", "mask", "tau")):
+        assert torch.equal(a, b), name

@@ -231,6 +231,11 @@ def workspace_views(ws: torch.Tensor, B: int, H: int, N: int, d: int) -> Dict[st
         "kcov": f32(lay.kcov, (B, H, d, d)),
         "qbar": f32(lay.qbar, (B, H, nb, d)),
     }
+    nw = (nb + 63) // 64
+    bf = lambda off, shape: ws[off:off + 2 * math.prod(shape)].view(torch.bfloat16).view(shape)
+    views["kbar_bf"] = bf(lay.kbar_bf, (B, H, nw, BLOCK, d))
+    views["vbar_t"] = bf(lay.vbar_t, (B, H, nw, d, BLOCK))
+    views["vbar_bf"] = bf(lay.vbar_bf, (B, H, nw, BLOCK, d))
     if ws.numel() >= lay.vt + 2 * B * H * N * d:   # not a low-memory workspace
         views["vt"] = ws[lay.vt:lay.vt + 2 * B * H * N * d].view(torch.bfloat16).view(B, H, nb, d, BLOCK)
     return views

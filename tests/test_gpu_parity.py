@@ -235,6 +235,39 @@ def test_prepass_summaries(w, gpu_lib):
             np.testing.assert_allclose(views["kcov"][b, h], C, rtol=0, atol=1e-5 * np.abs(C).max())
 
 
+TILE_CASES = [SMALL[1], SMALL[2], SMALL[5], CHUNK64,
+              wl.small("tiles_d128_65", 1, 3, 64 * 65, 128, grid=(1, 65, 64))]
+
+
+@pytest.mark.parametrize("lm", [False, True], ids=["default", "low_memory"])
+@pytest.mark.parametrize("w", TILE_CASES, ids=lambda w: w.name)
+def test_prepass_summary_tiles(w, lm, gpu_lib):
+    """The bf16 summary tiles (block correction, per-row correction) bit for bit: k_bar and
+    v_bar = vsum / 64 of the workspace's own fp32 summaries rounded to bf16, 64 key blocks per
+    tile, v_bar^T columns in the V^T key order, rows and columns past n_b zero; the row-major
+    v_bar tiles in the low-memory mode. The workspace is filled with a sentinel first, so any
+    entry the pre-pass leaves unwritten shows."""
+    flags = gpu_lib.SOL_LOW_MEMORY if lm else 0
+    q, k, v = wl.make_qkv(w)
+    ws = gpu_lib.new_workspace(w.B, w.H, w.N, w.d, flags=flags)
+    ws.fill_(0x7F)
+    gpu_lib.sol_block_summaries(k.cuda(), v.cuda(), ws, flags)
+    torch.cuda.synchronize()
+    raw = {n: t.cpu() for n, t in gpu_lib.workspace_views(ws, w.B, w.H, w.N, w.d).items()}
+    nb = w.n_blocks
+    nw = (nb + 63) // 64
+    pad = lambda x: torch.nn.functional.pad(x, (0, 0, 0, 64 * nw - nb))
+    kb = pad(raw["kbar"]).to(torch.bfloat16).view(w.B, w.H, nw, 64, w.d)
+    vb = pad(raw["vsum"] / 64).to(torch.bfloat16).view(w.B, w.H, nw, 64, w.d)
+    c = torch.arange(64)
+    g, sl = (c % 32) // 8, c % 8
+    key = 32 * (c // 32) + torch.where(sl < 4, 4 * g + sl, 16 + 4 * g + sl - 4)
+    assert torch.equal(raw["kbar_bf"], kb)
+    assert torch.equal(raw["vbar_t"], vb.transpose(-1, -2)[..., key])
+    if lm:
+        assert torch.equal(raw["vbar_bf"], vb)
+
+
 def test_item_clock_export(gpu_lib):
     """The optional work-item clock: one (start, end) pair per workgroup, at the entry of its
     first query block; workgroups take G consecutive blocks; other entries untouched."""

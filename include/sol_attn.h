@@ -88,8 +88,10 @@ typedef enum sol_status {
                                 A smaller workspace (sol_attn_workspace_bytes_flags); the
                                 same results bit for bit, some time more. Pass it to the
                                 pre-pass and to the fused pass alike: a workspace whose
-                                pre-pass ran with it holds no V^T for a pass without it.
-                                No effect for float32 inputs.                              */
+                                pre-pass ran with it holds no V^T for a pass without it,
+                                and one whose pre-pass ran without it holds no row-major
+                                v_bar tiles for a per-row-correction pass with it. Neither
+                                mismatch is detected. No effect for float32 inputs.        */
 #define SOL_FLAGS_ALL  0x3Fu
 
 /* Optional per-call outputs, all device pointers owned by the caller, each may be NULL.

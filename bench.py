@@ -438,6 +438,44 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def tile_mix(iters: int) -> int:
+    """The tile loop's instruction mix alone (csrc/tile_mix.hip): per step of 16 bf16 MFMAs
+    (v_mfma_f32_16x16x32_bf16, 16384 flop each), 0 to 16 LDS operand reads, 24 FMAs and 8
+    exponentials, with 1 or 2 waves per SIMD on every CU, each launch timed with HIP events.
+    Reports the MFMA rate, its fraction of the 2.5 PFLOP/s bf16 peak and of the pure-MFMA
+    mix's rate at two waves per SIMD."""
+    import ctypes
+    from free_block_sparse_mean_amd import build as _b
+    if not os.path.exists(_b.MIX_LIB):
+        print(f"{_b.MIX_LIB} is not built (python -m free_block_sparse_mean_amd.build)", file=sys.stderr)
+        return 2
+    lib = ctypes.CDLL(_b.MIX_LIB)
+    lib.sol_tile_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_int)]
+    lib.sol_tile_mix_shape.argtypes = [ctypes.c_int] + [ctypes.POINTER(ctypes.c_int)] * 3
+    rows = []
+    for wps in (2, 1):
+        for mix in range(6):
+            shape = [ctypes.c_int() for _ in range(3)]
+            if lib.sol_tile_mix_shape(mix, *[ctypes.byref(x) for x in shape]) != 0:
+                break
+            ms, cus = ctypes.c_double(), ctypes.c_int()
+            rc = lib.sol_tile_mix(mix, wps, iters, ctypes.byref(ms), ctypes.byref(cus))
+            if rc != 0:
+                print(f"sol_tile_mix(mix {mix}, {wps} waves per SIMD) failed: {rc}", file=sys.stderr)
+                return 1
+            mfmas = cus.value * 4 * wps * iters * 16
+            tflops = mfmas * 16384.0 / (ms.value * 1e-3) / 1e12
+            rows.append({"mix": mix, "waves_per_simd": wps, "lds_reads": shape[0].value,
+                         "fmas": shape[1].value, "exps": shape[2].value, "mfmas_per_step": 16,
+                         "ms": ms.value, "tflops": tflops, "frac_of_peak": tflops / PEAK_BF16_TFLOPS})
+    pure = next(r["tflops"] for r in rows if r["mix"] == 0 and r["waves_per_simd"] == 2)
+    for r in rows:
+        r["of_pure_mfma_rate"] = r["tflops"] / pure
+    print(json.dumps({"tile_mix": rows, "steps_per_wave": iters, "cus": cus.value}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -458,6 +496,9 @@ def main() -> int:
     ap.add_argument("--configs", default="c2_video_16k,c3_dit14b_77k,c5_batched_skewed_64k",
                     help="other configurations timed in the default run ('' for none)")
     ap.add_argument("--config-reps", type=int, default=5)
+    ap.add_argument("--tile-mix", action="store_true",
+                    help="only run the issue-rate microbenchmark of the tile loop's instruction mix "
+                         "(libsoltilemix.so) and print one JSON line")
     ap.add_argument("--sweep", default="",
                     help="comma list of bf16 configs to time at every beta they list (one JSON "
                          "line each) instead of the headline benchmark")
@@ -475,6 +516,9 @@ def main() -> int:
 
     if args.sweep:
         return sweep([x for x in args.sweep.split(",") if x], max(3, args.steps))
+
+    if args.tile_mix:
+        return tile_mix(20000)
 
     if args.copy_calibration:
         n = 512 * 2 ** 20

@@ -14,6 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsolattn.so")
 SOURCES = ["api.cpp", "prepass.hip", "fused.hip", "route.hip", "noalloc.hip"]
+# the tile loop's issue-rate microbenchmark (bench.py --tile-mix), not part of libsolattn.so
+MIX_LIB = os.path.join(PKG, "libsoltilemix.so")
+MIX_SOURCE = "tile_mix.hip"
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -65,7 +68,16 @@ def build(verbose: bool = False) -> str:
         if os.path.exists(row_obj):
             os.remove(row_obj)
     os.replace(tmp, LIB)
+    build_tile_mix(verbose)
     return LIB
+
+
+def build_tile_mix(verbose: bool = False) -> str:
+    """Compile the tile-loop microbenchmark into libsoltilemix.so; returns its path."""
+    tmp = MIX_LIB + ".tmp"
+    _run([hipcc(), *HIPCC_FLAGS, os.path.join(CSRC, MIX_SOURCE), "-o", tmp], verbose)   # the library's flags
+    os.replace(tmp, MIX_LIB)
+    return MIX_LIB
 
 
 if __name__ == "__main__":

@@ -133,3 +133,18 @@ def test_low_memory_f32_inputs(form, gpu_lib):
     low = _run(gpu_lib, q, k, v, 1.0, base | gpu_lib.SOL_LOW_MEMORY)
     for a, b, name in zip(ref, low, ("out", "kept", "mask", "tau")):
         assert torch.equal(a, b), name
+
+
+@pytest.mark.parametrize("form", ["block", "row"])
+def test_low_memory_max_sequence_length(form, gpu_lib):
+    """N = 262144 (n_b = 4096, the largest), two heads: one taken by the statically mapped
+    workgroups, one dealt from the work-item queue. The value tiles then lie up to 64 MiB
+    into each head's V; outputs, selections and row statistics bit for bit the default mode's."""
+    print(f"case low-memory max N {form}", flush=True)
+    w = wl.small("lm_max_n", 1, 2, 262144, 128, grid=(64, 64, 64))
+    q, k, v = (t.cuda() for t in wl.make_qkv(w))
+    base = gpu_lib.SOL_CORRECTION if form == "block" else gpu_lib.SOL_CORRECTION_ROW
+    ref = _run(gpu_lib, q, k, v, 1.5, base)
+    low = _run(gpu_lib, q, k, v, 1.5, base | gpu_lib.SOL_LOW_MEMORY)
+    for a, b, name in zip(ref, low, ("out", "kept", "mask", "tau")):
+        assert torch.equal(a, b), name

@@ -438,6 +438,36 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def dense_reference(q, k, v, w, reps: int):
+    """Dense softmax attention over the same tensors by PyTorch's own
+    scaled_dot_product_attention, restricted to its flash backend (it raises instead of
+    falling back to the N^2 math path): context for the dense-path ratios, not part of the
+    library. Returns the error text when the backend is unavailable."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    kernel = "torch.nn.functional.scaled_dot_product_attention, flash backend"
+    st = torch.cuda.current_stream()
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            o = torch.nn.functional.scaled_dot_product_attention(q, k, v)   # untimed
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+                o = torch.nn.functional.scaled_dot_product_attention(q, k, v)
+                b.record(st)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+        del o
+    except RuntimeError as e:
+        return {"kernel": kernel, "torch": torch.__version__, "error": str(e)[:300]}
+    flop = 4.0 * w.B * w.H * w.N * w.N * w.d
+    return {"kernel": kernel, "torch": torch.__version__, "reps": reps, "ms": statistics.median(ts),
+            "ms_min": min(ts), "tflops": flop / (min(ts) * 1e-3) / 1e12,
+            "frac_of_peak": flop / (min(ts) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def tile_mix(iters: int) -> int:
     """The tile loop's instruction mix alone (csrc/tile_mix.hip): per step of 16 bf16 MFMAs
     (v_mfma_f32_16x16x32_bf16, 16384 flop each), 0 to 16 LDS operand reads, 24 FMAs and 8
@@ -488,6 +518,8 @@ def main() -> int:
     ap.add_argument("--no-correction", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-routing-study", action="store_true")
+    ap.add_argument("--no-dense-reference", action="store_true",
+                    help="skip timing PyTorch's flash-backend dense attention on the same tensors")
     ap.add_argument("--no-calibration", action="store_true",
                     help="skip the beta calibrated to 5%% density (it runs the fused pass at many betas)")
     ap.add_argument("--cpu-blocks-per-head", type=int, default=96)
@@ -590,6 +622,11 @@ def main() -> int:
     lowmem["default_workspace_bytes"] = sb.sol_attn_workspace_bytes(w.B, w.H, w.N, w.d)
     lowmem["bit_equal_to_default"] = bool(torch.equal(out, ref))   # same beta and correction
     study = None if args.no_routing_study else routing_study(sb, qd, kd, vd, out, ws, w, 5)
+    dense_ref = None
+    if not args.no_dense_reference and w.dtype == "bf16":
+        dense_ref = dense_reference(qd, kd, vd, w, 3)
+        if "ms" in dense_ref:
+            dense_ref["fused_speedup_at_headline_beta"] = dense_ref["ms_min"] / head["fused_ms"]
     if study is not None:
         # like for like: the in-pass routing's cost inside the fused pass (fused pass without
         # the correction minus plain block-sparse attention on the same selection) against
@@ -658,6 +695,7 @@ def main() -> int:
         "routing_ablation": ablation,
         "row_correction": rowc,
         "low_memory": lowmem,
+        "dense_reference": dense_ref,
         "routing_study": study,
         "prepass": prepass_report(w, head["prepass_ms"]),
         "configs": configs,

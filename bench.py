@@ -460,8 +460,8 @@ def dense_reference(q, k, v, w, reps: int):
                 torch.cuda.synchronize()
                 ts.append(a.elapsed_time(b))
         del o
-    except RuntimeError as e:
-        return {"kernel": kernel, "torch": torch.__version__, "error": str(e)[:300]}
+    except Exception as e:   # context only: never let it end the benchmark
+        return {"kernel": kernel, "torch": torch.__version__, "error": f"{type(e).__name__}: {str(e)[:300]}"}
     flop = 4.0 * w.B * w.H * w.N * w.N * w.d
     return {"kernel": kernel, "torch": torch.__version__, "reps": reps, "ms": statistics.median(ts),
             "ms_min": min(ts), "tflops": flop / (min(ts) * 1e-3) / 1e12,

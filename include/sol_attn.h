@@ -215,7 +215,8 @@ sol_status sol_attn_fused_joint(const void* q, const void* k, const void* v, voi
  *                bits past n_b are ignored. A query block with no bit set gets
  *                zero output rows.
  *   kept_per_row [B*H*n_b] int32, device, optional (NULL): popcount of each row.
- * flags: SOL_F32 and SOL_SYNC only; SOL_CORRECTION or SOL_DENSE give
+ * flags: SOL_F32, SOL_SYNC and SOL_LOW_MEMORY (as on the pre-pass that filled
+ * the workspace); SOL_CORRECTION, SOL_CORRECTION_ROW or SOL_DENSE give
  * SOL_ERR_INVALID_ARG. Asynchronous on hip_stream like sol_attn_fused. */
 sol_status sol_attn_masked(const void* q, const void* k, const void* v, void* out,
                            int B, int H, int N, int d, const uint64_t* mask_bits,
@@ -246,7 +247,9 @@ sol_status sol_attn_masked(const void* q, const void* k, const void* v, void* ou
  *   kept_per_row device int32 [B*H*n_b] or NULL
  *   topk_idx     device int32 [B*H*n_b*top_k] or NULL: SOL_ROUTE_TOPK only, the kept
  *                key blocks of each row, best first (only min(top_k, n_b) written)
- * flags: SOL_F32 and SOL_SYNC only. Errors: NaN beta / top_p or negative top_k,
+ * flags: SOL_F32, SOL_SYNC and SOL_LOW_MEMORY (a workspace of that mode's size;
+ * routing reads no V^T); SOL_CORRECTION, SOL_CORRECTION_ROW or SOL_DENSE give
+ * SOL_ERR_INVALID_ARG. Errors: NaN beta / top_p or negative top_k,
  * unknown mode -> SOL_ERR_INVALID_ARG. The masks feed sol_attn_masked. */
 #define SOL_ROUTE_THRESHOLD 0
 #define SOL_ROUTE_TOPK      1

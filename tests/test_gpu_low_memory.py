@@ -92,16 +92,18 @@ def test_low_memory_given_mask_and_joint(gpu_lib):
     assert torch.equal(outs[0][1], outs[1][1])
 
 
-def test_low_memory_strided(gpu_lib):
+@pytest.mark.parametrize("form", ["none", "block", "row"])
+def test_low_memory_strided(form, gpu_lib):
     """[B, N, H, d] tensors in the low-memory mode: the value tiles come straight from the
-    strided V; bit for bit the contiguous default-mode result."""
+    strided V; bit for bit the contiguous default-mode result, for every correction form."""
     w = CASES[0]
     q, k, v = (t.cuda() for t in wl.make_qkv(w))
+    base = {"none": 0, "block": gpu_lib.SOL_CORRECTION, "row": gpu_lib.SOL_CORRECTION_ROW}[form]
     ref = torch.empty_like(q)
-    gpu_lib.sol_attn_fwd_ex(q, k, v, ref, 1.0, gpu_lib.SOL_CORRECTION)
+    gpu_lib.sol_attn_fwd_ex(q, k, v, ref, 1.0, base)
     qs, ks, vs = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v))
     out = torch.empty_like(qs)
-    gpu_lib.sol_attn_fwd_strided(qs, ks, vs, out, 1.0, gpu_lib.SOL_CORRECTION | gpu_lib.SOL_LOW_MEMORY)
+    gpu_lib.sol_attn_fwd_strided(qs, ks, vs, out, 1.0, base | gpu_lib.SOL_LOW_MEMORY)
     torch.cuda.synchronize()
     assert torch.equal(out.contiguous(), ref)
 
@@ -148,3 +150,31 @@ def test_low_memory_max_sequence_length(form, gpu_lib):
     low = _run(gpu_lib, q, k, v, 1.5, base | gpu_lib.SOL_LOW_MEMORY)
     for a, b, name in zip(ref, low, ("out", "kept", "mask", "tau")):
         assert torch.equal(a, b), name
+
+
+def test_low_memory_routing_baselines_and_masked(gpu_lib):
+    """The map-based routing baselines and the given-mask pass on a workspace of the
+    low-memory size (with the flag): the same proxy map, masks and outputs as on a full
+    workspace."""
+    w = CASES[0]
+    q, k, v = (t.cuda() for t in wl.make_qkv(w))
+    nb = w.n_blocks
+    W = (nb + 63) // 64
+    res = []
+    for flags in (0, gpu_lib.SOL_LOW_MEMORY):
+        ws = gpu_lib.new_workspace(w.B, w.H, w.N, w.d, q.device, flags)
+        assert ws.numel() == gpu_lib.sol_attn_workspace_bytes(w.B, w.H, w.N, w.d, flags)
+        gpu_lib.sol_block_summaries(k, v, ws, flags)
+        pm = torch.empty((w.B, w.H, nb, nb), dtype=torch.float32, device=q.device)
+        got = []
+        for mode, kw in ((gpu_lib.SOL_ROUTE_THRESHOLD, {"beta": 1.0}), (gpu_lib.SOL_ROUTE_TOPK, {"top_k": 9}),
+                         (gpu_lib.SOL_ROUTE_TOPP, {"top_p": 0.5})):
+            words = torch.zeros((w.B, w.H, nb, W), dtype=torch.int64, device=q.device)
+            gpu_lib.sol_route(q, mode, ws, pm, words, flags=flags, **kw)
+            out = torch.empty_like(q)
+            gpu_lib.sol_attn_masked(q, k, v, out, words, flags, ws)
+            torch.cuda.synchronize()
+            got += [pm.clone(), words, out]
+        res.append(got)
+    for a, b in zip(*res):
+        assert torch.equal(a, b)

@@ -178,3 +178,20 @@ def test_low_memory_routing_baselines_and_masked(gpu_lib):
         res.append(got)
     for a, b in zip(*res):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("N", [64, 128, 192, 64 * 65])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("form", ["block", "row"])
+def test_low_memory_tiny_and_word_edges(N, d, form, gpu_lib):
+    """One to 65 key blocks (a single partial tile, a tile plus one block): the low-memory
+    mode bit for bit the default mode, keep-all, threshold and keep-none."""
+    w = wl.small(f"lm_edge_{N}_{d}", 1, 2, N, d, grid=(1, N // 64, 64))
+    q, k, v = (t.cuda() for t in wl.make_qkv(w))
+    base = gpu_lib.SOL_CORRECTION if form == "block" else gpu_lib.SOL_CORRECTION_ROW
+    for beta in (-math.inf, 0.5, math.inf):
+        print(f"case low-memory edge N={N} d={d} {form} beta={beta}", flush=True)
+        ref = _run(gpu_lib, q, k, v, beta, base)
+        low = _run(gpu_lib, q, k, v, beta, base | gpu_lib.SOL_LOW_MEMORY)
+        for a, b, name in zip(ref, low, ("out", "kept", "mask", "tau")):
+            assert torch.equal(a, b), name
